@@ -1,0 +1,193 @@
+"""CPU oracle for exact scaled-dot-product attention (prefill, decode, MLA decode).
+
+TEST INFRASTRUCTURE ONLY.  This package is the slow, plain reference that the
+HIP kernels are checked against.  Only the test suite, the package smoke check
+and the benchmark's CPU-baseline leg may import it; the GPU library never does,
+and the two share no code.
+
+The arithmetic lives in ``attn_oracle.c`` (fp64, OpenMP over output rows),
+compiled with gcc into ``oracle/_build/libattn_oracle.so`` by :func:`build`.
+This module only marshals numpy arrays: inputs are widened to float32 (exact
+for the bf16 and fp32 inputs the kernels take) and results come back as
+float64.
+
+Pages the definitions follow (cited by title and section):
+  * "Attention Engineering: From MHA to GQA, MLA & FlashAttention", section 2
+    (GQA formulation), section 3 (MLA absorbed score and output), section 4
+    (online-softmax state and log-sum-exp), section 5 (KV-cache byte formula).
+  * "Attention deep dive (MHA -> MQA -> GQA -> FlashAttention)", section 5
+    (decode against the cache) and section 6 (sliding-window mask).
+  * "2.4 Multi-Head Attention, MQA, GQA & MLA", "Implementing the MHA -> GQA
+    conversion" (query head j reads KV group j // n_rep).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_BUILD_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD_DIR, "libattn_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (fp64, no fast-math, OpenMP)."""
+    os.makedirs(_BUILD_DIR, exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    D = ctypes.c_double
+    lib.oracle_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, D, P, I]
+    lib.oracle_prefill.restype = I
+    lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D]
+    lib.oracle_decode.restype = I
+    lib.oracle_mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, D]
+    lib.oracle_mla_decode.restype = I
+    lib.oracle_merge_partials.argtypes = [P, P, I, I, P, P]
+    lib.oracle_merge_partials.restype = None
+    lib.oracle_set_threads.argtypes = [I]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = I
+    _lib = lib
+    return lib
+
+
+def _f32(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != np.float32:
+        a = a.astype(np.float32)
+    return np.ascontiguousarray(a)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def prefill(q, k, v, *, causal: bool, window: int = 0, scale: float,
+            rows=None):
+    """Exact attention forward.
+
+    q:[B,hq,T,d]  k,v:[B,hkv,T,d].  ``rows`` optionally lists the query
+    positions to evaluate (all T when None).  Returns (o, lse):
+    o:[B,hq,n_rows,d] float64, lse:[B,hq,n_rows] float64 (natural log).
+    """
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, hq, T, d = q.shape
+    hkv = k.shape[1]
+    assert k.shape == (B, hkv, T, d) and v.shape == k.shape
+    if rows is None:
+        rows_arr, n_rows, rows_ptr = None, T, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        assert rows_arr.ndim == 1 and (rows_arr.size == 0 or (
+            rows_arr.min() >= 0 and rows_arr.max() < T))
+        n_rows, rows_ptr = int(rows_arr.size), _ptr(rows_arr)
+    o = np.zeros((B, hq, n_rows, d), dtype=np.float64)
+    lse = np.zeros((B, hq, n_rows), dtype=np.float64)
+    rc = _load().oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                B, T, hq, hkv, d, int(bool(causal)),
+                                int(window), float(scale), rows_ptr, n_rows)
+    if rc != 0:
+        raise ValueError("oracle_prefill: invalid shape")
+    return o, lse
+
+
+def decode(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale: float):
+    """Single-token decode.  q:[B,hq,d] (or [B,hq,1,d]),
+    caches:[B,hkv,S_max,d], seq_lens:[B].  Returns (o:[B,hq,d], lse:[B,hq])."""
+    q = _f32(q)
+    if q.ndim == 4:
+        q = np.ascontiguousarray(q[:, :, 0, :])
+    kc, vc = _f32(k_cache), _f32(v_cache)
+    B, hq, d = q.shape
+    _, hkv, S_max, _ = kc.shape
+    assert kc.shape == (B, hkv, S_max, d) and vc.shape == kc.shape
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    assert lens.shape == (B,)
+    o = np.zeros((B, hq, d), dtype=np.float64)
+    lse = np.zeros((B, hq), dtype=np.float64)
+    rc = _load().oracle_decode(_ptr(q), _ptr(kc), _ptr(vc), _ptr(lens),
+                               _ptr(o), _ptr(lse), B, S_max, hq, hkv, d,
+                               int(window), float(scale))
+    if rc != 0:
+        raise ValueError("oracle_decode: invalid shape")
+    return o, lse
+
+
+def mla_decode(q, cache, seq_lens, *, d_c: int, d_r: int, scale: float):
+    """MLA absorbed decode.  q:[B,H,d_c+d_r]  cache:[B,S_max,d_c+d_r].
+    Returns (o:[B,H,d_c], lse:[B,H])."""
+    q, c = _f32(q), _f32(cache)
+    B, H, dk = q.shape
+    assert dk == d_c + d_r and c.shape[0] == B and c.shape[2] == dk
+    S_max = c.shape[1]
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    assert lens.shape == (B,)
+    o = np.zeros((B, H, d_c), dtype=np.float64)
+    lse = np.zeros((B, H), dtype=np.float64)
+    rc = _load().oracle_mla_decode(_ptr(q), _ptr(c), _ptr(lens), _ptr(o),
+                                   _ptr(lse), B, S_max, H, d_c, d_r,
+                                   float(scale))
+    if rc != 0:
+        raise ValueError("oracle_mla_decode: invalid shape")
+    return o, lse
+
+
+def merge_partials(parts_o, parts_lse):
+    """Merge normalised partial results over disjoint key sets.
+    parts_o:[n,dv] parts_lse:[n] -> (o:[dv], lse)."""
+    po = np.ascontiguousarray(np.asarray(parts_o, dtype=np.float64))
+    pl = np.ascontiguousarray(np.asarray(parts_lse, dtype=np.float64))
+    n, dv = po.shape
+    assert pl.shape == (n,)
+    o = np.zeros(dv, dtype=np.float64)
+    lse = np.zeros(1, dtype=np.float64)
+    _load().oracle_merge_partials(_ptr(po), _ptr(pl), n, dv, _ptr(o), _ptr(lse))
+    return o, float(lse[0])
+
+
+def kv_cache_bytes(B: int, S: int, L: int, n_kv: int, d_h: int,
+                   b_bytes: int) -> int:
+    """KV-cache footprint M_KV = 2 * B * S * L * (n_kv * d_h) * b_bytes
+    ("Attention Engineering ...", section 0, equation "KV-Cache Memory
+    Footprint & Arithmetic Intensity")."""
+    return 2 * B * S * L * (n_kv * d_h) * b_bytes
+
+
+def mla_cache_bytes(B: int, S: int, L: int, d_c: int, d_r: int,
+                    b_bytes: int) -> int:
+    """MLA cache: d_c + d_R scalars per token per layer ("Attention
+    Engineering ...", section 3, text after the complete MLA score)."""
+    return B * S * L * (d_c + d_r) * b_bytes

@@ -1,0 +1,276 @@
+/*
+ * attn_oracle.c -- the CPU oracle for exact scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct
+ * reference that the HIP kernels are checked against.  Only the test suite,
+ * the package smoke check and the benchmark's CPU-baseline leg may load it.
+ * It shares no code, header, table or helper with the GPU library, and the
+ * GPU library never calls it.
+ *
+ * Everything is computed in IEEE double precision from the exact input
+ * values (bf16 and fp32 inputs arrive widened to float, which is exact).
+ * No blocking, tiling, online rescaling or reordering beyond the plain
+ * definition: each score row is materialised in full, masked, soft-maxed
+ * and used to mix the values.  Built without -ffast-math.
+ *
+ * Sources (the pages the method is taken from):
+ *  - "Attention Engineering: From MHA to GQA, MLA & FlashAttention",
+ *    section 2, equation "Grouped-Query Attention Formulation":
+ *    O = softmax(Q K^T / sqrt(d_h) + M) V per query head, with the query
+ *    heads of group g sharing K_g and V_g.
+ *  - "2.4 Multi-Head Attention, MQA, GQA & MLA", section "Implementing the
+ *    MHA -> GQA conversion": query head j reads KV group floor(j / n_rep).
+ *  - "Attention deep dive (MHA -> MQA -> GQA -> FlashAttention)", section 6
+ *    "Sliding-window attention": key j is visible to query i iff
+ *    (j <= i) and (i - j < W).
+ *  - "Attention Engineering ...", section 4, the FlashAttention-2 recurrence
+ *    and its epilogue: the per-row log-sum-exp L = m + log(l).
+ *  - "Attention deep dive ...", section 5 "The KV cache": at decode the one
+ *    new query attends to every cached key (cached + new), so no causal
+ *    mask applies inside the cache.
+ *  - "Attention Engineering ...", section 3, equation "Complete MLA
+ *    Attention Score": s = (q_absorbed . c + q_R . k_R) / sqrt(d_h + d_R),
+ *    and the absorbed output sum_s alpha_s c_s before W_UV.
+ *
+ * Conventions (readings where the pages leave a step open):
+ *  - the caller passes the softmax scale (1/sqrt(d_h) for plain attention,
+ *    1/sqrt(d_h + d_R) for MLA); it multiplies the dot product before the
+ *    mask and the softmax;
+ *  - a masked entry is excluded from the softmax (a select, not an added
+ *    -inf), so a non-finite value at a masked key never reaches the result;
+ *  - a row with no visible key has output 0 and log-sum-exp -inf;
+ *  - the log-sum-exp is the natural logarithm.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Visibility of key j to query i for the prefill mask.  Causal: j <= i.
+ * Window W > 0: additionally i - j < W ("Attention deep dive", section 6). */
+static int prefill_visible(long i, long j, int causal, int window)
+{
+    if (causal && j > i) return 0;
+    if (window > 0 && i - j >= window) return 0;
+    return 1;
+}
+
+/* softmax over the visible entries of s[0..n), then out[d] = sum_j p_j v_j[d].
+ * v_row(j) points at the value row of key j (stride vstride floats).
+ * Writes out[0..dv) and *lse. */
+static void softmax_mix(const double *s, const unsigned char *vis, long n,
+                        const float *v, long vstride, int dv,
+                        double *out, double *lse, double *p)
+{
+    double m = -INFINITY;
+    long any = 0;
+    for (long j = 0; j < n; ++j)
+        if (vis[j]) { if (!any || s[j] > m) m = s[j]; any = 1; }
+    for (int d = 0; d < dv; ++d) out[d] = 0.0;
+    if (!any) { *lse = -INFINITY; return; }
+    double l = 0.0;
+    for (long j = 0; j < n; ++j) {
+        p[j] = vis[j] ? exp(s[j] - m) : 0.0;
+        l += p[j];
+    }
+    for (long j = 0; j < n; ++j) {
+        if (!vis[j]) continue;
+        const double w = p[j] / l;
+        const float *vr = v + j * vstride;
+        for (int d = 0; d < dv; ++d) out[d] += w * (double)vr[d];
+    }
+    *lse = m + log(l);
+}
+
+/*
+ * Prefill forward.  q:[B,hq,T,d]  k,v:[B,hkv,T,d]  (row-major, float).
+ * rows: optional list of n_rows query positions to evaluate (NULL = all T,
+ * in order).  o:[B,hq,n_rows,d]  lse:[B,hq,n_rows] (may be NULL).
+ * Query head h reads KV head h / (hq / hkv).
+ * Returns 0, or -1 for an invalid shape.
+ */
+int oracle_prefill(const float *q, const float *k, const float *v,
+                   double *o, double *lse,
+                   int B, int T, int hq, int hkv, int d,
+                   int causal, int window, double scale,
+                   const int *rows, int n_rows)
+{
+    if (B < 0 || T < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv) return -1;
+    if (!rows) n_rows = T;
+    const int G = hq / hkv;
+    const long units = (long)B * hq * n_rows;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (T > 0 ? T : 1));
+        double *p = (double *)malloc(sizeof(double) * (T > 0 ? T : 1));
+        unsigned char *vis = (unsigned char *)malloc(T > 0 ? T : 1);
+#pragma omp for schedule(dynamic, 16)
+        for (long u = 0; u < units; ++u) {
+            const long r = u % n_rows;
+            const long h = (u / n_rows) % hq;
+            const long b = u / ((long)n_rows * hq);
+            const long i = rows ? rows[r] : r;
+            const long g = h / G;
+            const float *qi = q + (((b * hq + h) * T) + i) * d;
+            const float *kb = k + ((b * hkv + g) * (long)T) * d;
+            const float *vb = v + ((b * hkv + g) * (long)T) * d;
+            /* full score row, then the mask */
+            for (long j = 0; j < T; ++j) {
+                double acc = 0.0;
+                const float *kj = kb + j * d;
+                for (int t = 0; t < d; ++t) acc += (double)qi[t] * (double)kj[t];
+                s[j] = acc * scale;
+                vis[j] = (unsigned char)prefill_visible(i, j, causal, window);
+            }
+            double l_out;
+            softmax_mix(s, vis, T, vb, d, d, o + u * d, &l_out, p);
+            if (lse) lse[u] = l_out;
+        }
+        free(s); free(p); free(vis);
+    }
+    return 0;
+}
+
+/*
+ * Single-token decode against a KV cache.
+ * q:[B,hq,d]  kc,vc:[B,hkv,S_max,d]  seq_lens[B] (valid cached length of
+ * sequence b, already including the current token).  The query is the
+ * token at position len-1; it sees cache positions j < len, and with a
+ * window W > 0 only those with (len-1) - j < W.
+ * o:[B,hq,d]  lse:[B,hq] (may be NULL).
+ */
+int oracle_decode(const float *q, const float *kc, const float *vc,
+                  const int *seq_lens, double *o, double *lse,
+                  int B, int S_max, int hq, int hkv, int d,
+                  int window, double scale)
+{
+    if (B < 0 || S_max < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv) return -1;
+    const int G = hq / hkv;
+    const long units = (long)B * hq;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (S_max > 0 ? S_max : 1));
+        double *p = (double *)malloc(sizeof(double) * (S_max > 0 ? S_max : 1));
+        unsigned char *vis = (unsigned char *)malloc(S_max > 0 ? S_max : 1);
+#pragma omp for schedule(dynamic, 1)
+        for (long u = 0; u < units; ++u) {
+            const long h = u % hq, b = u / hq, g = h / G;
+            long len = seq_lens[b];
+            if (len < 0) len = 0;
+            if (len > S_max) len = S_max;
+            const long i = len - 1;
+            const float *qi = q + (b * hq + h) * (long)d;
+            const float *kb = kc + ((b * hkv + g) * (long)S_max) * d;
+            const float *vb = vc + ((b * hkv + g) * (long)S_max) * d;
+            for (long j = 0; j < len; ++j) {
+                double acc = 0.0;
+                const float *kj = kb + j * d;
+                for (int t = 0; t < d; ++t) acc += (double)qi[t] * (double)kj[t];
+                s[j] = acc * scale;
+                vis[j] = (unsigned char)(window <= 0 || i - j < window);
+            }
+            double l_out;
+            softmax_mix(s, vis, len, vb, d, d, o + u * d, &l_out, p);
+            if (lse) lse[u] = l_out;
+        }
+        free(s); free(p); free(vis);
+    }
+    return 0;
+}
+
+/*
+ * MLA absorbed-latent decode.
+ * q:[B,H,dc+dr]: per head the absorbed content query (first dc entries)
+ *   followed by the rotated decoupled query (last dr entries).
+ * cache:[B,S_max,dc+dr]: per token the latent c (first dc) followed by the
+ *   shared rotated key k_R (last dr).
+ * s_j = scale * (q[0:dc] . c_j + q[dc:] . kR_j); o = sum_j softmax_j c_j,
+ * i.e. the latent context before the W_UV up-projection.
+ * o:[B,H,dc]  lse:[B,H] (may be NULL).
+ */
+int oracle_mla_decode(const float *q, const float *cache, const int *seq_lens,
+                      double *o, double *lse,
+                      int B, int S_max, int H, int dc, int dr, double scale)
+{
+    if (B < 0 || S_max < 0 || H <= 0 || dc <= 0 || dr < 0) return -1;
+    const int dk = dc + dr;
+    const long units = (long)B * H;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (S_max > 0 ? S_max : 1));
+        double *p = (double *)malloc(sizeof(double) * (S_max > 0 ? S_max : 1));
+        unsigned char *vis = (unsigned char *)malloc(S_max > 0 ? S_max : 1);
+#pragma omp for schedule(dynamic, 1)
+        for (long u = 0; u < units; ++u) {
+            const long b = u / H;
+            long len = seq_lens[b];
+            if (len < 0) len = 0;
+            if (len > S_max) len = S_max;
+            const float *qh = q + u * (long)dk;
+            const float *cb = cache + b * (long)S_max * dk;
+            for (long j = 0; j < len; ++j) {
+                const float *cj = cb + j * dk;
+                double content = 0.0, rope = 0.0;
+                for (int t = 0; t < dc; ++t) content += (double)qh[t] * (double)cj[t];
+                for (int t = 0; t < dr; ++t) rope += (double)qh[dc + t] * (double)cj[dc + t];
+                s[j] = (content + rope) * scale;
+                vis[j] = 1;
+            }
+            double l_out;
+            softmax_mix(s, vis, len, cb, dk, dc, o + u * dc, &l_out, p);
+            if (lse) lse[u] = l_out;
+        }
+        free(s); free(p); free(vis);
+    }
+    return 0;
+}
+
+/*
+ * Merge of partial attention results over disjoint key sets.
+ * Each part s carries a normalised output O_s (over its own keys) and its
+ * log-sum-exp L_s.  The union's result follows from the FlashAttention-2
+ * state ("Attention Engineering ...", section 4): L = log sum_s exp(L_s),
+ * O = sum_s exp(L_s - L) O_s.  Parts with L_s = -inf (no keys) drop out.
+ * parts_o:[n_parts,dv]  parts_lse:[n_parts]  ->  o:[dv], *lse.
+ */
+void oracle_merge_partials(const double *parts_o, const double *parts_lse,
+                           int n_parts, int dv, double *o, double *lse)
+{
+    double m = -INFINITY;
+    for (int s = 0; s < n_parts; ++s)
+        if (parts_lse[s] > m) m = parts_lse[s];
+    for (int t = 0; t < dv; ++t) o[t] = 0.0;
+    if (m == -INFINITY) { *lse = -INFINITY; return; }
+    double z = 0.0;
+    for (int s = 0; s < n_parts; ++s)
+        if (parts_lse[s] != -INFINITY) z += exp(parts_lse[s] - m);
+    const double L = m + log(z);
+    for (int s = 0; s < n_parts; ++s) {
+        if (parts_lse[s] == -INFINITY) continue;
+        const double w = exp(parts_lse[s] - L);
+        for (int t = 0; t < dv; ++t) o[t] += w * parts_o[(long)s * dv + t];
+    }
+    *lse = L;
+}
+
+/* Threads the OpenMP regions above use (0 leaves the runtime default). */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
