@@ -1,0 +1,154 @@
+/*
+ * mi355attn.h -- C ABI of libmi355attn.so: exact scaled-dot-product attention
+ * with grouped K/V heads on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (for every query head h of a batch entry b):
+ *
+ *     O[h] = softmax( scale * Q[h] K[g]^T  (+ mask) ) V[g],   g = h / (h_q / h_kv)
+ *
+ * the grouped-query form in "Attention Engineering: From MHA to GQA, MLA &
+ * FlashAttention", section 2 (equation "Grouped-Query Attention
+ * Formulation"), with consecutive query heads sharing one K/V head ("2.4
+ * Multi-Head Attention, MQA, GQA & MLA", "Implementing the MHA -> GQA
+ * conversion").  h_kv == h_q is MHA, h_kv == 1 is MQA.  The S x S score
+ * matrix is never written to memory: the kernels stream K/V tiles and keep
+ * the online-softmax state (running max m, running sum l, unnormalised
+ * output) in registers, dividing by l once at the end ("Attention
+ * Engineering ...", section 4, the FlashAttention-2 recurrence).
+ *
+ * Conventions shared by every entry point
+ *  - All tensors are dense, row-major ("contiguous"), in device memory of the
+ *    current HIP device, and owned by the caller.  The library allocates,
+ *    frees and synchronises nothing; every call only enqueues work on
+ *    `stream` and returns.  A workspace, where one is needed, is caller
+ *    memory of at least the size the matching *_workspace_size() returns.
+ *  - `scale` multiplies Q.K before masking and softmax (1/sqrt(d_h) for plain
+ *    attention; 1/sqrt(d_h + d_R) for MLA).  Masked keys are excluded from
+ *    the softmax (they are never read into the result, whatever they hold).
+ *  - Accumulation (m, l, output, log-sum-exp) is fp32.  For bf16 inputs the
+ *    softmax weights are rounded to bf16 as the operand of the P.V product;
+ *    outputs are rounded to bf16 (round-to-nearest-even).
+ *  - `lse`, where offered, receives the natural-log log-sum-exp of the
+ *    scaled, masked score row, L = m + ln(l); it may be NULL.  A row with no
+ *    visible key gets O = 0 and L = -inf.
+ *  - Inputs are checked on the host before anything is launched.  Failures
+ *    return a status and enqueue nothing.  ATTN_ERR_HIP reports a launch
+ *    error from the HIP runtime (hipGetLastError after the launch).
+ *  - Calls on different streams may run concurrently; calls that share a
+ *    workspace must be ordered by the caller.
+ */
+#ifndef MI355ATTN_H
+#define MI355ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,   /* null pointer, bad size, h_q % h_kv != 0, window without causal, non-finite scale */
+    ATTN_ERR_UNSUPPORTED = 2,   /* a head size / dtype / head count with no kernel instantiated */
+    ATTN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than *_workspace_size() */
+    ATTN_ERR_HIP = 4            /* the HIP runtime rejected a launch */
+} attn_status_t;
+
+typedef enum {
+    ATTN_F32 = 0,               /* IEEE float32 */
+    ATTN_BF16 = 1               /* bfloat16 (1-8-7) */
+} attn_dtype_t;
+
+/*
+ * attn_prefill -- prefill / training forward over a whole sequence.
+ *
+ *   q   : [B, h_q,  T, d_h]   dtype            (read)
+ *   k, v: [B, h_kv, T, d_h]   dtype            (read)
+ *   o   : [B, h_q,  T, d_h]   dtype            (written)
+ *   lse : [B, h_q,  T]        float32 or NULL  (written)
+ *
+ * Visibility of key j to query i (queries and keys share positions 0..T-1):
+ *   causal != 0 : j <= i                              ("Attention Engineering ...", section 2 listing: upper-triangular -inf mask)
+ *   window  > 0 : additionally i - j < window         ("Attention deep dive (MHA -> MQA -> GQA -> FlashAttention)", section 6)
+ * window > 0 requires causal != 0.  causal == 0 with window == 0 is full
+ * (bidirectional) attention.
+ *
+ * Supported: dtype ATTN_BF16 with d_h = 128 (MFMA kernel); dtype ATTN_F32
+ * with d_h in {16, 32, 64, 128}.  Any B >= 1, T >= 1, h_q a multiple of h_kv.
+ */
+attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
+                           float *lse, int B, int T, int h_q, int h_kv, int d_h,
+                           attn_dtype_t dtype, int causal, int window, float scale,
+                           hipStream_t stream);
+
+/*
+ * attn_decode -- one new query token per sequence against a bf16 KV cache
+ * ("Attention deep dive ...", section 5 "The KV cache": the new query
+ * attends to every cached key, cached + new, so no causal mask applies
+ * inside the cache).
+ *
+ *   q        : [B, h_q, d_h]          bf16   (read; a [B,h_q,1,d_h] tensor has this layout)
+ *   k_cache  : [B, h_kv, S_max, d_h]  bf16   (read; only positions < seq_lens[b])
+ *   v_cache  : [B, h_kv, S_max, d_h]  bf16   (read; only positions < seq_lens[b])
+ *   o        : [B, h_q, d_h]          bf16   (written)
+ *   lse      : [B, h_q]               float32 or NULL (written)
+ *   seq_lens : [B]                    int32, device memory; the valid cache
+ *              length of sequence b, including the current token.  Values are
+ *              clamped to [0, S_max]; a zero length gives o = 0, lse = -inf.
+ *
+ * window > 0 restricts the query (position seq_lens[b]-1) to the last
+ * `window` cached keys.  The cache is split into chunks of `split_tokens`
+ * positions (0 = the library's choice; otherwise a positive multiple of
+ * 64), each chunk is attended to independently and the partial results are
+ * merged with their log-sum-exp weights; the split changes only rounding.
+ * Supported: d_h = 128, any h_q that is a multiple of h_kv.
+ */
+size_t attn_decode_workspace_size(int B, int S_max, int h_q, int h_kv, int d_h,
+                                  int split_tokens);
+attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                          void *o, float *lse, const int32_t *seq_lens,
+                          int B, int S_max, int h_q, int h_kv, int d_h,
+                          int window, float scale, int split_tokens,
+                          void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * mla_decode -- Multi-head Latent Attention decode with the up-projections
+ * absorbed ("Attention Engineering ...", section 3, equations "Associative
+ * Weight Absorption Identity" and "Complete MLA Attention Score").
+ *
+ *   q        : [B, h_q, d_c + d_r]     bf16  (read) per head the absorbed content
+ *              query W_UK^T q_C (first d_c) then the rotated RoPE query (last d_r)
+ *   kv_cache : [B, S_max, d_c + d_r]   bf16  (read) per token the latent c_KV
+ *              (first d_c) then the shared rotated RoPE key k_R (last d_r)
+ *   o        : [B, h_q, d_c]           bf16  (written) sum_j softmax_j c_j, the
+ *              latent context before the caller applies W_UV
+ *   lse      : [B, h_q]                float32 or NULL (written)
+ *   seq_lens : [B] int32, device memory, clamped to [0, S_max].
+ *
+ * score_j = scale * (q[:d_c] . c_j + q[d_c:] . kR_j); the value of token j
+ * is the first d_c entries of the same cache row.  split_tokens as for
+ * attn_decode.  Supported: d_c = 512, d_r = 64, h_q a multiple of 16.
+ */
+size_t mla_decode_workspace_size(int B, int S_max, int h_q, int d_c, int d_r,
+                                 int split_tokens);
+attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *lse,
+                         const int32_t *seq_lens, int B, int S_max, int h_q,
+                         int d_c, int d_r, float scale, int split_tokens,
+                         void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *attn_status_string(attn_status_t status);
+
+/* ABI version of this header (bumped on incompatible change). */
+#define MI355ATTN_ABI_VERSION 1
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355ATTN_H */

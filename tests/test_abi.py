@@ -1,0 +1,117 @@
+"""The C-ABI library builds, loads and exports what include/*.h declares, and
+its host-side validation rejects bad arguments before any launch (CPU only:
+no call here reaches the GPU)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                             text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import transformer_attention_amd as ta
+    return ta.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("attn_prefill", "attn_decode", "mla_decode", "attn_decode_workspace_size",
+              "mla_decode_workspace_size", "attn_status_string", "attn_abi_version"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared_functions():
+        assert hasattr(lib, n), f"symbol {n} declared in include/ but not exported"
+
+
+def test_status_strings(lib):
+    import transformer_attention_amd as ta
+    assert ta.status_string(0) == "ok"
+    for s in range(1, 5):
+        assert ta.status_string(s) not in ("ok", "unknown status")
+    assert lib.attn_abi_version() == 1
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, T=16, hq=4, hkv=2, d=128,
+             dtype=1, causal=1, window=0, scale=0.1)
+    a.update(kw)
+    return lib.attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["T"], a["hq"],
+                            a["hkv"], a["d"], a["dtype"], a["causal"], a["window"], a["scale"], None)
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, q=None) == 1
+    assert _prefill(lib, o=None) == 1
+    assert _prefill(lib, B=0) == 1
+    assert _prefill(lib, T=-1) == 1
+    assert _prefill(lib, hq=6, hkv=4) == 1          # h_q must be a multiple of h_kv
+    assert _prefill(lib, window=-1) == 1
+    assert _prefill(lib, window=8, causal=0) == 1   # window needs causal
+    assert _prefill(lib, scale=float("nan")) == 1
+    assert _prefill(lib, scale=float("inf")) == 1
+    assert _prefill(lib, d=64) == 2                 # bf16 kernel is d = 128
+    assert _prefill(lib, dtype=0, d=48) == 2        # fp32 d not instantiated
+    assert _prefill(lib, dtype=7) == 2
+
+
+def test_decode_validation(lib):
+    def dec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lens=FAKE, B=2, S=64, hq=8, hkv=2, d=128,
+                 window=0, scale=0.1, split=0, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.attn_decode(a["q"], a["k"], a["v"], a["o"], None, a["lens"], a["B"], a["S"],
+                               a["hq"], a["hkv"], a["d"], a["window"], a["scale"], a["split"],
+                               a["ws"], a["wsb"], None)
+    assert dec(lens=None) == 1
+    assert dec(hq=7) == 1
+    assert dec(window=-3) == 1
+    assert dec(split=100) == 1                      # not a multiple of 64
+    assert dec(d=64) == 2
+    assert dec(ws=None) == 3
+    need = lib.attn_decode_workspace_size(2, 64, 8, 2, 128, 0)
+    assert need > 0
+    assert dec(wsb=need - 1) == 3
+    assert lib.attn_decode_workspace_size(2, 64, 7, 2, 128, 0) == 0
+
+
+def test_mla_validation(lib):
+    def mla(**kw):
+        a = dict(q=FAKE, c=FAKE, o=FAKE, lens=FAKE, B=2, S=64, H=128, dc=512, dr=64, scale=0.07,
+                 split=0, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.mla_decode(a["q"], a["c"], a["o"], None, a["lens"], a["B"], a["S"], a["H"],
+                              a["dc"], a["dr"], a["scale"], a["split"], a["ws"], a["wsb"], None)
+    assert mla(c=None) == 1
+    assert mla(scale=float("nan")) == 1
+    assert mla(split=32) == 1
+    assert mla(dc=256) == 2
+    assert mla(H=24) == 2
+    assert mla(ws=None) == 3
+    need = lib.mla_decode_workspace_size(2, 64, 128, 512, 64, 0)
+    assert mla(wsb=need - 1) == 3
+
+
+def test_workspace_grows_with_splits(lib):
+    a = lib.attn_decode_workspace_size(4, 4096, 16, 2, 128, 64)
+    b = lib.attn_decode_workspace_size(4, 4096, 16, 2, 128, 1024)
+    assert a > b > 0

@@ -1,0 +1,232 @@
+"""Python binding of libmi355attn.so (exact GQA/MQA/MHA attention on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/mi355attn.h``.  PyTorch
+provides device memory and the current stream; the functions below check
+tensor shapes/dtypes/devices, pass raw pointers, and raise
+:class:`AttnError` on a non-OK status.  There is no CPU fallback: if the
+library is not built, importing the entry points raises.
+
+Entry points (same names as the C ABI):
+  attn_prefill(q, k, v, *, causal, window=0, scale=None, o=None, lse=None)
+  attn_decode(q, k_cache, v_cache, seq_lens, *, window=0, scale=None,
+              split_tokens=0, o=None, lse=None, workspace=None)
+  mla_decode(q, kv_cache, seq_lens, *, d_c=512, d_r=64, scale,
+             split_tokens=0, o=None, lse=None, workspace=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmi355attn.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_WORKSPACE = 3
+ATTN_ERR_HIP = 4
+ATTN_F32 = 0
+ATTN_BF16 = 1
+
+EXPORTED_SYMBOLS = (
+    "attn_prefill", "attn_decode", "attn_decode_workspace_size",
+    "mla_decode", "mla_decode_workspace_size", "attn_status_string",
+    "attn_abi_version",
+)
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m transformer_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+    lib.attn_prefill.restype = I
+    lib.attn_decode_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.attn_decode_workspace_size.restype = Z
+    lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.attn_decode.restype = I
+    lib.mla_decode_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.mla_decode_workspace_size.restype = Z
+    lib.mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, Z, P]
+    lib.mla_decode.restype = I
+    lib.attn_status_string.argtypes = [I]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = I
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, name, dtype, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_DT = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+
+
+def attn_prefill(q, k, v, *, causal: bool = True, window: int = 0, scale=None,
+                 o=None, lse=None, return_lse: bool = False):
+    """q:[B,h_q,T,d]  k,v:[B,h_kv,T,d] (bf16 or fp32, contiguous, same device).
+    Returns o (and lse:[B,h_q,T] fp32 when requested)."""
+    lib = load_library()
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _require(q, "q", q.dtype, ndim=4)
+    _require(k, "k", q.dtype, q.device, 4)
+    _require(v, "v", q.dtype, q.device, 4)
+    B, hq, T, d = q.shape
+    hkv = k.shape[1]
+    if tuple(k.shape) != (B, hkv, T, d) or tuple(v.shape) != (B, hkv, T, d):
+        raise ValueError("k/v shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    _require(o, "o", q.dtype, q.device)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o shape mismatch")
+    if lse is None and return_lse:
+        lse = torch.empty((B, hq, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, q.device)
+        if lse.numel() != B * hq * T:
+            raise ValueError("lse shape mismatch")
+    st = lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, hq,
+                          hkv, d, _DT[q.dtype], int(bool(causal)), int(window),
+                          float(scale), _stream(q.device))
+    _check(st, "attn_prefill")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_decode_workspace_size(B, S_max, h_q, h_kv, d_h, split_tokens=0) -> int:
+    return int(load_library().attn_decode_workspace_size(B, S_max, h_q, h_kv, d_h,
+                                                         split_tokens))
+
+
+def attn_decode(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale=None,
+                split_tokens: int = 0, o=None, lse=None, workspace=None,
+                return_lse: bool = False):
+    """q:[B,h_q,d] or [B,h_q,1,d] bf16; caches:[B,h_kv,S_max,d] bf16;
+    seq_lens: int32[B] on the device.  Returns o shaped like q."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16)
+    _require(k_cache, "k_cache", torch.bfloat16, q.device, 4)
+    _require(v_cache, "v_cache", torch.bfloat16, q.device, 4)
+    _require(seq_lens, "seq_lens", torch.int32, q.device, 1)
+    B, hkv, S_max, d = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("v_cache shape mismatch")
+    hq = q.shape[1]
+    if q.numel() != B * hq * d or q.shape[0] != B or q.shape[-1] != d:
+        raise ValueError("q shape mismatch")
+    if seq_lens.shape[0] != B:
+        raise ValueError("seq_lens shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    _require(o, "o", torch.bfloat16, q.device)
+    if o.numel() != q.numel():
+        raise ValueError("o shape mismatch")
+    if lse is None and return_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, q.device)
+    need = lib.attn_decode_workspace_size(B, S_max, hq, hkv, d, int(split_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", None, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
+                         _ptr(seq_lens), B, S_max, hq, hkv, d, int(window),
+                         float(scale), int(split_tokens), _ptr(workspace), ws_bytes,
+                         _stream(q.device))
+    _check(st, "attn_decode")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def mla_decode_workspace_size(B, S_max, h_q, d_c=512, d_r=64, split_tokens=0) -> int:
+    return int(load_library().mla_decode_workspace_size(B, S_max, h_q, d_c, d_r,
+                                                        split_tokens))
+
+
+def mla_decode(q, kv_cache, seq_lens, *, d_c: int = 512, d_r: int = 64, scale: float,
+               split_tokens: int = 0, o=None, lse=None, workspace=None,
+               return_lse: bool = False):
+    """q:[B,H,d_c+d_r] bf16; kv_cache:[B,S_max,d_c+d_r] bf16; seq_lens int32[B].
+    Returns o:[B,H,d_c] bf16 (the latent context before W_UV)."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16, ndim=3)
+    _require(kv_cache, "kv_cache", torch.bfloat16, q.device, 3)
+    _require(seq_lens, "seq_lens", torch.int32, q.device, 1)
+    B, H, dk = q.shape
+    if dk != d_c + d_r or kv_cache.shape[0] != B or kv_cache.shape[2] != dk:
+        raise ValueError("q / kv_cache shape mismatch")
+    S_max = kv_cache.shape[1]
+    if o is None:
+        o = torch.empty((B, H, d_c), dtype=torch.bfloat16, device=q.device)
+    _require(o, "o", torch.bfloat16, q.device)
+    if o.numel() != B * H * d_c:
+        raise ValueError("o shape mismatch")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, q.device)
+    need = lib.mla_decode_workspace_size(B, S_max, H, d_c, d_r, int(split_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", None, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.mla_decode(_ptr(q), _ptr(kv_cache), _ptr(o), _ptr(lse), _ptr(seq_lens),
+                        B, S_max, H, d_c, d_r, float(scale), int(split_tokens),
+                        _ptr(workspace), ws_bytes, _stream(q.device))
+    _check(st, "mla_decode")
+    return (o, lse) if (return_lse or lse is not None) else o

@@ -1,0 +1,146 @@
+// api.hip -- the C ABI of libmi355attn.so (declared in include/mi355attn.h):
+// argument validation, workspace sizing and kernel dispatch.  No allocation,
+// no synchronisation: every entry point validates on the host, then enqueues
+// on the caller's stream and returns.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/mi355attn.h"
+#include "kernels.h"
+
+namespace {
+
+// Default split of the cache for decode, in keys.  Each split is one
+// workgroup's work; the choice trades enough workgroups to fill 256 CUs
+// against the partial-result traffic of the merge.
+int default_decode_split(int B, int S_max, int hkv, int G) {
+    const long long groups = (long long)B * hkv * ((G + 15) / 16);
+    int split = 512;
+    // grow the split while the grid stays > ~4 waves of workgroups over 256 CUs
+    while (split < 4096 && groups * ((S_max + 2 * split - 1) / (2 * split)) >= 4096) split *= 2;
+    return split;
+}
+
+int default_mla_split(int B, int S_max, int H) {
+    const long long chunks = (long long)B * ((H + 127) / 128);
+    int split = 256;
+    while (split < 8192 && chunks * ((S_max + 2 * split - 1) / (2 * split)) >= 512) split *= 2;
+    return split;
+}
+
+bool bad_ptr(const void *p) { return p == nullptr; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t split_ws_bytes(long long rows, long long n_split, long long dv) {
+    return align_up((size_t)(rows * n_split * dv) * sizeof(float), 256) +
+           align_up((size_t)(rows * n_split) * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return MI355ATTN_ABI_VERSION; }
+
+const char *attn_status_string(attn_status_t s) {
+    switch (s) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_INVALID_ARG: return "invalid argument";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+        case ATTN_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int B, int T, int h_q, int h_kv, int d_h, attn_dtype_t dtype,
+                           int causal, int window, float scale, hipStream_t stream) {
+    if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(o)) return ATTN_ERR_INVALID_ARG;
+    if (B <= 0 || T <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
+    if (h_q % h_kv != 0) return ATTN_ERR_INVALID_ARG;
+    if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+    if ((long long)B * h_q * T * d_h >= (1LL << 40)) return ATTN_ERR_UNSUPPORTED;
+    mi355::PrefillArgs a{q, k, v, o, lse, B, T, h_q, h_kv, d_h, causal ? 1 : 0, window, scale};
+    hipError_t e;
+    if (dtype == ATTN_BF16) {
+        if (d_h != 128) return ATTN_ERR_UNSUPPORTED;
+        e = mi355::launch_prefill_bf16_d128(a, stream);
+    } else if (dtype == ATTN_F32) {
+        if (d_h != 16 && d_h != 32 && d_h != 64 && d_h != 128) return ATTN_ERR_UNSUPPORTED;
+        if (h_q > 65535 || B > 65535) return ATTN_ERR_UNSUPPORTED;
+        e = mi355::launch_prefill_f32(a, stream);
+    } else {
+        return ATTN_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+static int resolve_decode_split(int split_tokens, int B, int S_max, int h_q, int h_kv) {
+    if (split_tokens == 0) return default_decode_split(B, S_max, h_kv, h_q / h_kv);
+    return split_tokens;
+}
+
+size_t attn_decode_workspace_size(int B, int S_max, int h_q, int h_kv, int d_h, int split_tokens) {
+    if (B <= 0 || S_max <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0 || h_q % h_kv) return 0;
+    if (split_tokens < 0 || split_tokens % 64) return 0;
+    const int split = resolve_decode_split(split_tokens, B, S_max, h_q, h_kv);
+    const long long ns = (S_max + split - 1) / split;
+    return split_ws_bytes((long long)B * h_q, ns, d_h);
+}
+
+attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *o,
+                          float *lse, const int32_t *seq_lens, int B, int S_max, int h_q,
+                          int h_kv, int d_h, int window, float scale, int split_tokens,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (bad_ptr(q) || bad_ptr(k_cache) || bad_ptr(v_cache) || bad_ptr(o) || bad_ptr(seq_lens))
+        return ATTN_ERR_INVALID_ARG;
+    if (B <= 0 || S_max <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
+    if (h_q % h_kv != 0 || window < 0 || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+    if (split_tokens < 0 || split_tokens % 64) return ATTN_ERR_INVALID_ARG;
+    if (d_h != 128) return ATTN_ERR_UNSUPPORTED;
+    if (B > 65535 || h_kv * ((h_q / h_kv + 15) / 16) > 65535) return ATTN_ERR_UNSUPPORTED;
+    const int split = resolve_decode_split(split_tokens, B, S_max, h_q, h_kv);
+    const int ns = (S_max + split - 1) / split;
+    const size_t need = attn_decode_workspace_size(B, S_max, h_q, h_kv, d_h, split_tokens);
+    if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    float *ws_o = static_cast<float *>(workspace);
+    float *ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                              align_up((size_t)B * h_q * ns * d_h * sizeof(float), 256));
+    mi355::DecodeArgs a{q, k_cache, v_cache, o, lse, seq_lens, B, S_max, h_q, h_kv, d_h,
+                        window, scale, split, ns, ws_o, ws_lse};
+    return mi355::launch_decode_bf16_d128(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t mla_decode_workspace_size(int B, int S_max, int h_q, int d_c, int d_r, int split_tokens) {
+    if (B <= 0 || S_max <= 0 || h_q <= 0 || d_c <= 0 || d_r < 0) return 0;
+    if (split_tokens < 0 || split_tokens % 64) return 0;
+    const int split = split_tokens ? split_tokens : default_mla_split(B, S_max, h_q);
+    const long long ns = (S_max + split - 1) / split;
+    return split_ws_bytes((long long)B * h_q, ns, d_c);
+}
+
+attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *lse,
+                         const int32_t *seq_lens, int B, int S_max, int h_q, int d_c, int d_r,
+                         float scale, int split_tokens, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    if (bad_ptr(q) || bad_ptr(kv_cache) || bad_ptr(o) || bad_ptr(seq_lens)) return ATTN_ERR_INVALID_ARG;
+    if (B <= 0 || S_max <= 0 || h_q <= 0 || d_c <= 0 || d_r < 0) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(scale) || split_tokens < 0 || split_tokens % 64) return ATTN_ERR_INVALID_ARG;
+    if (d_c != 512 || d_r != 64 || h_q % 16 != 0) return ATTN_ERR_UNSUPPORTED;
+    if (B > 65535) return ATTN_ERR_UNSUPPORTED;
+    const int split = split_tokens ? split_tokens : default_mla_split(B, S_max, h_q);
+    const int ns = (S_max + split - 1) / split;
+    const size_t need = mla_decode_workspace_size(B, S_max, h_q, d_c, d_r, split_tokens);
+    if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    float *ws_o = static_cast<float *>(workspace);
+    float *ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                              align_up((size_t)B * h_q * ns * d_c * sizeof(float), 256));
+    mi355::MlaArgs a{q, kv_cache, o, lse, seq_lens, B, S_max, h_q, d_c, d_r, scale, split, ns,
+                     ws_o, ws_lse};
+    return mi355::launch_mla_decode_bf16(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

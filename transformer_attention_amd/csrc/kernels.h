@@ -1,0 +1,60 @@
+// kernels.h -- host-side launchers of the gfx950 attention kernels (internal
+// to libmi355attn.so; the public ABI is include/mi355attn.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mi355 {
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int B, T, hq, hkv, d;
+    int causal, window;
+    float scale;
+};
+
+// bf16, d = 128, bf16 MFMA.  Returns hipSuccess or the launch error.
+hipError_t launch_prefill_bf16_d128(const PrefillArgs &a, hipStream_t stream);
+// fp32, d in {16, 32, 64, 128}, fp32 FMA.
+hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+    const void *q, *k_cache, *v_cache;
+    void *o;
+    float *lse;
+    const int32_t *seq_lens;
+    int B, S_max, hq, hkv, d;
+    int window;
+    float scale;
+    int split;            // keys per work item (multiple of 64)
+    int n_split_max;      // ceil(S_max / split)
+    float *ws_o;          // [B, hq, n_split_max, d]
+    float *ws_lse;        // [B, hq, n_split_max]  (log2 units)
+};
+hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream);
+
+struct MlaArgs {
+    const void *q, *cache;
+    void *o;
+    float *lse;
+    const int32_t *seq_lens;
+    int B, S_max, H, d_c, d_r;
+    float scale;
+    int split;
+    int n_split_max;
+    float *ws_o;          // [B, H, n_split_max, d_c]
+    float *ws_lse;        // [B, H, n_split_max]  (log2 units)
+};
+hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream);
+
+// Merge of split partials: o[b,h,:] (bf16) and lse[b,h] (natural log, may be
+// null) from ws_o/ws_lse over the ceil(len_b / split) splits of sequence b.
+hipError_t launch_split_combine(const float *ws_o, const float *ws_lse,
+                                const int32_t *seq_lens, void *o, float *lse,
+                                int B, int H, int dv, int S_max, int split,
+                                int n_split_max, hipStream_t stream);
+
+}  // namespace mi355

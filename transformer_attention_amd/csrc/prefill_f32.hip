@@ -1,0 +1,122 @@
+// prefill_f32.hip -- attention forward for fp32 inputs (d_h in {16,32,64,128}).
+//
+// Same method as the bf16 kernel -- K/V tiles staged on chip, a running
+// max / sum / unnormalised output per query row, one division at the end
+// ("Attention Engineering: From MHA to GQA, MLA & FlashAttention", section 4,
+// the FlashAttention-2 recurrence) -- but with fp32 FMAs throughout so that
+// fp32 inputs keep fp32 accuracy.  One thread owns one query row; a
+// workgroup of 64 threads covers 64 rows of one query head and reads the K/V
+// head h / (h_q / h_kv).  This path serves small fp32 problems; it is not
+// the throughput path.
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace mi355 {
+namespace {
+
+constexpr int ROWS = 64;
+constexpr int TK = 32;          // keys per LDS tile
+
+struct Params {
+    const float *q, *k, *v;
+    float *o;
+    float *lse;
+    int T, hq, hkv, G;
+    int causal, window;
+    float scale_log2;
+};
+
+template <int DH>
+__global__ __launch_bounds__(ROWS) void prefill_f32_kernel(Params p) {
+    __shared__ float ks[TK][DH];
+    __shared__ float vs[TK][DH];
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x * ROWS + tid;
+    const int h = blockIdx.y;
+    const int b = blockIdx.z;
+    const int g = h / p.G;
+    const int T = p.T;
+    const size_t q_base = ((size_t)b * p.hq + h) * (size_t)T * DH;
+    const size_t kv_base = ((size_t)b * p.hkv + g) * (size_t)T * DH;
+
+    float q[DH], o[DH];
+#pragma unroll
+    for (int d = 0; d < DH; ++d) {
+        q[d] = row < T ? p.q[q_base + (size_t)row * DH + d] : 0.f;
+        o[d] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+
+    const int r0 = blockIdx.x * ROWS;
+    const int kend = p.causal ? min(T, r0 + ROWS) : T;
+    const int kbeg = p.window > 0 ? max(0, r0 - p.window + 1) : 0;
+    for (int ts = (kbeg / TK) * TK; ts < kend; ts += TK) {
+        for (int c = tid; c < TK * DH; c += ROWS) {
+            const int j = c / DH, d = c % DH;
+            const int key = ts + j;
+            ks[j][d] = key < T ? p.k[kv_base + (size_t)key * DH + d] : 0.f;
+            vs[j][d] = key < T ? p.v[kv_base + (size_t)key * DH + d] : 0.f;
+        }
+        __syncthreads();
+        if (row < T) {
+            for (int j = 0; j < TK; ++j) {
+                const int key = ts + j;
+                bool vis = key < T;
+                if (p.causal) vis = vis && key <= row;
+                if (p.window > 0) vis = vis && (row - key) < p.window;
+                if (!vis) continue;
+                float s = 0.f;
+#pragma unroll
+                for (int d = 0; d < DH; ++d) s = fmaf(q[d], ks[j][d], s);
+                const float x = s * p.scale_log2;
+                if (x > m) {
+                    const float alpha = fast_exp2(m - x);
+                    l *= alpha;
+#pragma unroll
+                    for (int d = 0; d < DH; ++d) o[d] *= alpha;
+                    m = x;
+                }
+                const float pw = fast_exp2(x - m);
+                l += pw;
+#pragma unroll
+                for (int d = 0; d < DH; ++d) o[d] = fmaf(pw, vs[j][d], o[d]);
+            }
+        }
+        __syncthreads();
+    }
+    if (row >= T) return;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) p.o[q_base + (size_t)row * DH + d] = o[d] * inv;
+    if (p.lse)
+        p.lse[((size_t)b * p.hq + h) * (size_t)T + row] = l > 0.f ? m * kLn2 + __logf(l) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t stream) {
+    Params p;
+    p.q = static_cast<const float *>(a.q);
+    p.k = static_cast<const float *>(a.k);
+    p.v = static_cast<const float *>(a.v);
+    p.o = static_cast<float *>(a.o);
+    p.lse = a.lse;
+    p.T = a.T;
+    p.hq = a.hq;
+    p.hkv = a.hkv;
+    p.G = a.hq / a.hkv;
+    p.causal = a.causal;
+    p.window = a.window;
+    p.scale_log2 = a.scale * kLog2e;
+    dim3 grid((a.T + ROWS - 1) / ROWS, a.hq, a.B);
+    switch (a.d) {
+        case 16: hipLaunchKernelGGL(prefill_f32_kernel<16>, grid, dim3(ROWS), 0, stream, p); break;
+        case 32: hipLaunchKernelGGL(prefill_f32_kernel<32>, grid, dim3(ROWS), 0, stream, p); break;
+        case 64: hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(ROWS), 0, stream, p); break;
+        case 128: hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(ROWS), 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mi355
