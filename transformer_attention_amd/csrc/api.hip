@@ -10,22 +10,25 @@
 
 namespace {
 
-// Default split of the cache for decode, in keys.  Each split is one
-// workgroup's work; the choice trades enough workgroups to fill 256 CUs
-// against the partial-result traffic of the merge.
+// Default split of the cache for decode, in keys (a multiple of the 64-key
+// tile).  Each split is one workgroup; the choice keeps several workgroups
+// per CU for full-length sequences while each one still streams many tiles.
 int default_decode_split(int B, int S_max, int hkv, int G) {
     const long long groups = (long long)B * hkv * ((G + 15) / 16);
-    int split = 512;
-    // grow the split while the grid stays > ~4 waves of workgroups over 256 CUs
-    while (split < 4096 && groups * ((S_max + 2 * split - 1) / (2 * split)) >= 4096) split *= 2;
+    int split = 4096;
+    while (split > 256 && groups * ((S_max + split - 1) / split) < 2048) split /= 2;
     return split;
 }
 
+// MLA: one workgroup per (sequence, 128-head chunk, split); aim at one
+// workgroup per CU (256 CUs) for full-length sequences.
 int default_mla_split(int B, int S_max, int H) {
     const long long chunks = (long long)B * ((H + 127) / 128);
-    int split = 256;
-    while (split < 8192 && chunks * ((S_max + 2 * split - 1) / (2 * split)) >= 512) split *= 2;
-    return split;
+    long long split = (S_max * chunks + 255) / 256;
+    split = (split + 63) / 64 * 64;
+    if (split < 64) split = 64;
+    if (split > S_max) split = (S_max + 63) / 64 * 64;
+    return (int)split;
 }
 
 bool bad_ptr(const void *p) { return p == nullptr; }

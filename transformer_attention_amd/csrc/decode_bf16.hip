@@ -13,26 +13,23 @@
 // each cached K/V byte exactly once, coalesced, with many bytes in flight.
 //
 // The cache of each (sequence, K/V head) is cut into chunks of `split` keys;
-// one workgroup handles one chunk for all query heads of the group (up to 16
-// per workgroup), so every K/V byte is read once.  Inside a workgroup each of
-// the 4 waves streams 32-key blocks:
-//  * S^T = K q^T with v_mfma_f32_16x16x32_bf16: K rows go straight from global
-//    memory into the A operand (16-byte loads), q is held in registers as the
-//    B operand (the group's heads are the 16 columns);
-//  * the 16x16 D layout gives each lane four keys of one head; the two
-//    16-key blocks are assigned keys so that each lane's eight probabilities
-//    are eight consecutive keys, which makes P^T directly the B operand of
-//    O^T = V^T P^T;
-//  * V is written transposed into a wave-private LDS area (coalesced 16-byte
-//    global loads of key pairs, 32-bit LDS writes) and read back as 16-byte
-//    A operands;
-//  * the next block's K/V loads are issued before the current block is
-//    consumed.
-// The running (m, l, O) of the four waves are merged through LDS and the
-// chunk's normalised partial output and log-sum-exp are written to the
-// workspace; a second kernel merges the chunks of each (sequence, head):
-// L = log sum_s exp(L_s), O = sum_s exp(L_s - L) O_s, which is the
-// FlashAttention-2 state merge ("Attention Engineering ...", section 4).
+// one workgroup handles one chunk for up to 16 query heads of the group, so
+// every K/V byte of the chunk is read from HBM once:
+//  * 64-key tiles of K and V stream HBM -> LDS through a 4-stage ring filled
+//    by global_load_lds_dwordx4 (three tiles in flight per CU, no staging
+//    registers); rows are stored with a 304-byte stride (19 = 3 mod 16 bank
+//    slots), so 16-byte reads down a column and transposing reads of 4 rows
+//    are bank-conflict free and all addresses are base + immediate;
+//  * each of the 4 waves computes the whole score tile S^T = K q^T
+//    (v_mfma_f32_16x16x32_bf16, the group's heads as the 16 columns) and the
+//    softmax -- MFMA time is small next to the tile's HBM time, and doing it
+//    redundantly gives every wave the same (m, l) with no exchange -- then
+//    the P.V product for its own quarter of d: O^T = V^T P^T, with V^T read
+//    by ds_read_b64_tr_b16 and the rounded probabilities as the B operand;
+//  * the chunk's normalised partial output and log-sum-exp go to the
+//    workspace; a second kernel merges the chunks of each (sequence, head):
+//    L = log sum_s exp(L_s), O = sum_s exp(L_s - L) O_s, the FlashAttention-2
+//    state merge ("Attention Engineering ...", section 4).
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -40,10 +37,13 @@ namespace mi355 {
 namespace {
 
 constexpr int D = 128;
-constexpr int KB = 32;          // keys per wave step
-constexpr int NW = 4;           // waves per workgroup
-constexpr int VTS = KB + 8;     // LDS row stride of V^T, bf16 elements (80 B)
-constexpr int VT_WAVE = D * VTS;  // bf16 elements per wave
+constexpr int BN = 64;                    // keys per tile
+constexpr int NW = 4;                     // waves per workgroup
+constexpr int LROW = D * 2 + 48;          // LDS row stride, bytes (304)
+constexpr int REGION = BN * LROW;         // 19456 B: K rows, then V rows
+constexpr int TILE_BYTES = 2 * REGION;    // 38912 B = 38 one-KB DMA blocks
+constexpr int NSTAGE = 4;
+constexpr int LDS_BYTES = NSTAGE * TILE_BYTES;   // 155648
 constexpr float TAU = 8.0f;
 
 struct Params {
@@ -55,13 +55,15 @@ struct Params {
     float scale_log2;
 };
 
-__global__ __launch_bounds__(256) void decode_bf16_d128_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) __bf16 smem[NW * VT_WAVE];   // 40 KB
+__device__ __forceinline__ int tile_off(int r, int chunk) { return r * LROW + (chunk << 4); }
+
+__global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int c16 = lane & 15;
-    const int grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int j16 = lane & 15;
+    const int q16 = lane >> 4;
 
     const int s = blockIdx.x;
     const int g = blockIdx.y / p.n_hchunk;
@@ -73,102 +75,91 @@ __global__ __launch_bounds__(256) void decode_bf16_d128_kernel(Params p) {
     const int kvis = p.window > 0 ? max(0, len - p.window) : 0;
     const int lo = max(s * p.split, kvis);
     const int hi = min((s + 1) * p.split, len);
+    const int n_tiles = lo < hi ? (hi - lo + BN - 1) / BN : 0;
 
-    const int hidx = hc * 16 + c16;                       // head within the group
+    const int hidx = hc * 16 + j16;                       // head within the group (column)
     const bool head_ok = hidx < p.G;
     const int h = g * p.G + hidx;
+    const size_t kv_base = ((size_t)b * p.hkv + g) * (size_t)p.S_max * D;
+    const char *kg = reinterpret_cast<const char *>(p.k + kv_base);
+    const char *vg = reinterpret_cast<const char *>(p.v + kv_base);
 
-    // q^T as B operand: column = head, K = d (four quarters of 32).
+    // DMA of tile t: blocks 0-18 fill the K rows, 19-37 the V rows; waves 0-1
+    // issue 10 blocks, waves 2-3 issue 9.  LDS byte o of a region holds row
+    // o / 304, chunk (o % 304) / 16; pad slots receive an arbitrary valid
+    // chunk, rows past the chunk end re-read the last valid key (masked).
+    const int my_blk0 = wave < 2 ? 10 * wave : 20 + 9 * (wave - 2);
+    const int my_nblk = wave < 2 ? 10 : 9;
+    auto issue_tile = [&](int t) {
+        char *stage = smem + (t % NSTAGE) * TILE_BYTES;
+        const int t0 = lo + t * BN;
+#pragma unroll
+        for (int i = 0; i < 10; ++i) {
+            if (i >= my_nblk) break;
+            const int blk = my_blk0 + i;
+            const int o = blk * 1024 + lane * 16;
+            const bool is_v = o >= REGION;
+            const int ro = is_v ? o - REGION : o;
+            const int r = ro / LROW;
+            const int ch = min((ro - r * LROW) >> 4, D / 8 - 1);
+            const int key = min(t0 + r, hi - 1);
+            const char *src = (is_v ? vg : kg) + (size_t)key * (D * 2) + ch * 16;
+            dma16(src, stage + blk * 1024);
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < NSTAGE - 1; ++t)
+        if (t < n_tiles) issue_tile(t);
+
+    // q^T as B operand: column = head j16, d = 32ks + 8 q16 .. +7.
     bf16x8 qop[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         u32x4 val = {0u, 0u, 0u, 0u};
-        if (head_ok) val = ldg16(p.q + ((size_t)b * p.hq + h) * D + 32 * ks + 8 * grp);
+        if (head_ok) val = ldg16(p.q + ((size_t)b * p.hq + h) * D + 32 * ks + 8 * q16);
         qop[ks] = __builtin_bit_cast(bf16x8, val);
     }
 
-    const size_t kv_base = ((size_t)b * p.hkv + g) * (size_t)p.S_max * D;
-    const __bf16 *kg = p.k + kv_base;
-    const __bf16 *vg = p.v + kv_base;
-    __bf16 *vt = smem + wave * VT_WAVE;
-    uint32_t *vt32 = reinterpret_cast<uint32_t *>(vt);
-
-    f32x4 oacc[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 oacc[2];                                        // d = 32 wave + 16 dbl + 4 q16 + i
+    oacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    oacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    const int v_row_lane = 4 * q16 + (j16 >> 2);
+    const int v_chunk_lane = 4 * wave + ((j16 & 3) >> 1);  // chunk of d = 32 wave + 16 dbl + 4(j%4)
+    const int v_byte_lane = 8 * (j16 & 1);
 
-    // Register staging of one 32-key block starting at kb0.
-    // K: A operand for block mb, quarter ks: lane row r = c16 holds key
-    //    kb0 + 8*(r>>2) + 4*mb + (r&3), d = 32ks + 8grp.
-    // V: key pairs (2pr, 2pr+1), pr = grp + 4j, chunk c16.
-    u32x4 kreg[2][4], vreg[4][2];
-    auto load_block = [&](int kb0) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int key = kb0 + 8 * (c16 >> 2) + 4 * mb + (c16 & 3);
-            const bool ok = key >= lo && key < hi;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                u32x4 val = {0u, 0u, 0u, 0u};
-                if (ok) val = ldg16(kg + (size_t)key * D + 32 * ks + 8 * grp);
-                kreg[mb][ks] = val;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int key = kb0 + 2 * (grp + 4 * j) + e;
-                u32x4 val = {0u, 0u, 0u, 0u};
-                if (key >= lo && key < hi) val = ldg16(vg + (size_t)key * D + 8 * c16);
-                vreg[j][e] = val;
-            }
-    };
+    for (int t = 0; t < n_tiles; ++t) {
+        const int newer = t == 0 ? 0 : min(NSTAGE - 2, n_tiles - 1 - t);
+        if (newer == 0) wait_vmcnt<0>();
+        else if (newer == 1) { if (my_nblk == 10) wait_vmcnt<10>(); else wait_vmcnt<9>(); }
+        else { if (my_nblk == 10) wait_vmcnt<20>(); else wait_vmcnt<18>(); }
+        raw_barrier();
+        if (t + NSTAGE - 1 < n_tiles) issue_tile(t + NSTAGE - 1);
 
-    // blocks handled by this wave: kb0 = lo + KB * (wave + NW * n)
-    int kb0 = lo + KB * wave;
-    if (kb0 < hi) load_block(kb0);
-    for (; kb0 < hi; kb0 += KB * NW) {
-        // V^T into the wave's LDS area (rotated element order spreads banks)
+        const char *kt = smem + (t % NSTAGE) * TILE_BYTES;
+        const char *vt = kt + REGION;
+        const int t0 = lo + t * BN;
+        // S^T blocks mb = 0..3: key 16mb + j16 (A row), element (mb, i) of this
+        // lane = key t0 + 16mb + 4 q16 + i of head column j16.
+        f32x4 sacc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int pr = grp + 4 * j;
-            const u32x4 a = vreg[j][0], bq = vreg[j][1];
-#pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const int e = (st + c16) & 7;
-                const uint32_t wa = a[e >> 1], wb = bq[e >> 1];
-                const uint32_t packed = (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u))
-                                                : ((wa & 0xffffu) | (wb << 16));
-                vt32[((8 * c16 + e) * VTS) / 2 + pr] = packed;
-            }
-        }
-        bf16x8 kop[2][4];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) kop[mb][ks] = __builtin_bit_cast(bf16x8, kreg[mb][ks]);
-        const int cur = kb0;
-        if (kb0 + KB * NW < hi) load_block(kb0 + KB * NW);
-
-        f32x4 sacc[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 4; ++mb) {
             sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) sacc[mb] = mfma16x16x32(kop[mb][ks], qop[ks], sacc[mb]);
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + tile_off(16 * mb + j16, 4 * ks + q16));
+                sacc[mb] = mfma16x16x32(a, qop[ks], sacc[mb]);
+            }
         }
-        // element (mb, i) of this lane is key cur + 8*grp + 4*mb + i
-        float x[8];
+        const bool tail = t0 + BN > hi;
+        float x[16];
         float mx = -INFINITY;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = cur + 8 * grp + 4 * mb + i;
                 float v = sacc[mb][i] * p.scale_log2;
-                v = (key >= lo && key < hi) ? v : -INFINITY;
+                if (tail) v = (t0 + 16 * mb + 4 * q16 + i < hi) ? v : -INFINITY;
                 x[4 * mb + i] = v;
                 mx = fmaxf(mx, v);
             }
@@ -178,83 +169,43 @@ __global__ __launch_bounds__(256) void decode_bf16_d128_kernel(Params p) {
         const float m_new = upd ? mx : m_run;
         const float alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
         m_run = m_new;
-        if (__any(upd)) {
-#pragma unroll
-            for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
-        }
+        oacc[0] *= alpha;
+        oacc[1] *= alpha;
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        float pv[8];
+        float pv[16];
         float lsum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 16; ++e) {
             pv[e] = fast_exp2(x[e] - m_use);
             lsum += pv[e];
         }
         l_run = l_run * alpha + lsum;
-        const bf16x8 pop = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // K-step kk covers keys 32kk .. 32kk+31: elements (mb = 2kk, i) then (2kk+1, i)
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vt + (16 * db + c16) * VTS + 8 * grp);
-            oacc[db] = mfma16x16x32(a, pop, oacc[db]);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    // Per-wave state: m_run (same in all lanes of a column), l partial per lane.
-    l_run += shfl_xor(l_run, 16);
-    l_run += shfl_xor(l_run, 32);
-
-    // Merge the four waves through LDS (reusing the V^T area).
-    __syncthreads();
-    float *red = reinterpret_cast<float *>(smem);        // [NW][16 heads][D] + m, l
-    float *red_m = red + NW * 16 * D;
-    float *red_l = red_m + NW * 16;
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 pop = to_bf16x8(pv[8 * kk + 0], pv[8 * kk + 1], pv[8 * kk + 2], pv[8 * kk + 3],
+                                         pv[8 * kk + 4], pv[8 * kk + 5], pv[8 * kk + 6], pv[8 * kk + 7]);
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d = 16 * db + 4 * grp + i;
-            red[(wave * 16 + c16) * D + d] = oacc[db][i];
-        }
-    if (grp == 0) {
-        red_m[wave * 16 + c16] = m_run;
-        red_l[wave * 16 + c16] = l_run;
-    }
-    __syncthreads();
-    // 256 threads: head = tid >> 4 (16 heads), d-range (tid & 15) * 8 .. +7
-    {
-        const int hh = tid >> 4;
-        const int d0 = (tid & 15) * 8;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w * 16 + hh]);
-        const float Mu = (M == -INFINITY) ? 0.f : M;
-        float L = 0.f, wgt[NW];
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            wgt[w] = fast_exp2(red_m[w * 16 + hh] - Mu);
-            L += wgt[w] * red_l[w * 16 + hh];
-        }
-        const float inv = L > 0.f ? 1.0f / L : 0.f;
-        const int hidx2 = hc * 16 + hh;
-        if (hidx2 < p.G) {
-            const int h2 = g * p.G + hidx2;
-            const size_t ws = (((size_t)b * p.hq + h2) * p.n_split_max + s);
-            float *wo = p.ws_o + ws * D;
-#pragma unroll
-            for (int dd = 0; dd < 8; ++dd) {
-                float acc = 0.f;
-#pragma unroll
-                for (int w = 0; w < NW; ++w) acc += wgt[w] * red[(w * 16 + hh) * D + d0 + dd];
-                wo[d0 + dd] = acc * inv;
+            for (int dbl = 0; dbl < 2; ++dbl) {
+                const int r = 32 * kk + v_row_lane;
+                const int ch = v_chunk_lane + 2 * dbl;
+                const bf16x4 lo4 = lds_read_tr16(vt + tile_off(r, ch) + v_byte_lane);
+                const bf16x4 hi4 = lds_read_tr16(vt + tile_off(r + 16, ch) + v_byte_lane);
+                const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[dbl] = mfma16x16x32(a, pop, oacc[dbl]);
             }
-            if ((tid & 15) == 0) p.ws_lse[ws] = L > 0.f ? Mu + __log2f(L) : -INFINITY;
         }
     }
+    float lt = l_run + shfl_xor(l_run, 16);
+    lt += shfl_xor(lt, 32);
+    if (!head_ok) return;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const size_t ws = ((size_t)b * p.hq + h) * p.n_split_max + s;
+    float *wo = p.ws_o + ws * D;
+#pragma unroll
+    for (int dbl = 0; dbl < 2; ++dbl)
+        *reinterpret_cast<f32x4 *>(wo + 32 * wave + 16 * dbl + 4 * q16) = oacc[dbl] * inv;
+    if (wave == 0 && q16 == 0) p.ws_lse[ws] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
 }
 
 // One wave per (head, sequence): merge the partials of the sequence's splits.
@@ -311,8 +262,15 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
     p.n_split_max = a.n_split_max;
     p.window = a.window;
     p.scale_log2 = a.scale * kLog2e;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)decode_bf16_d128_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
     dim3 grid(a.n_split_max, a.hkv * p.n_hchunk, a.B);
-    hipLaunchKernelGGL(decode_bf16_d128_kernel, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(decode_bf16_d128_kernel, grid, dim3(64 * NW), LDS_BYTES, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_combine(a.ws_o, a.ws_lse, a.seq_lens, a.o, a.lse, a.B, a.hq, D, a.S_max,

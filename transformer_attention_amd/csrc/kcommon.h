@@ -64,6 +64,48 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N & 0x30) << 10) | (0x7 << 4) | (0xF << 8));
+}
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// drain every outstanding global->LDS load); the asm statements keep the
+// compiler from moving memory accesses across it.  Callers order LDS
+// accesses themselves with wait_vmcnt / the lgkmcnt waits the compiler emits.
+__device__ __forceinline__ void raw_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// LDS byte offset of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char *)p);
+}
+// 16-byte global -> LDS copy (global_load_lds_dwordx4): lane L of the wave
+// writes bytes [16L, 16L+16) after the wave-uniform LDS address `lds_base`.
+// Issued through asm so the compiler does not treat every later LDS read as
+// possibly aliasing the copy (it would wait for all outstanding copies, i.e.
+// drain the prefetch ring); callers order the copies themselves with
+// wait_vmcnt and a barrier.  The instruction has no register results (its
+// address registers are read at issue), and nothing else in these kernels
+// uses m0.
+__device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_offset(lds_base));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gsrc), "s"(m0v) : "memory");
+}
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+// ds_read_b64_tr_b16: within each 16-lane group, result lane i element r is
+// the (i%4)-th bf16 of the 8 bytes addressed by lane 4r + i/4 of that group.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void *lds_ptr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_t *)((__attribute__((address_space(3))) char *)lds_ptr));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)p;
 }
