@@ -23,8 +23,10 @@
  *    `stream` and returns.  A workspace, where one is needed, is caller
  *    memory of at least the size the matching *_workspace_size() returns.
  *  - `scale` multiplies Q.K before masking and softmax (1/sqrt(d_h) for plain
- *    attention; 1/sqrt(d_h + d_R) for MLA).  Masked keys are excluded from
- *    the softmax (they are never read into the result, whatever they hold).
+ *    attention; 1/sqrt(d_h + d_R) for MLA); it must be finite and > 0.
+ *    Masked keys get weight exactly 0.  Cache positions outside a sequence's
+ *    visible range are never read.  Inside a prefill tile, a masked key's
+ *    values must be finite (they are multiplied by the weight 0).
  *  - Accumulation (m, l, output, log-sum-exp) is fp32.  For bf16 inputs the
  *    softmax weights are rounded to bf16 as the operand of the P.V product;
  *    outputs are rounded to bf16 (round-to-nearest-even).
@@ -50,7 +52,7 @@ extern "C" {
 
 typedef enum {
     ATTN_OK = 0,
-    ATTN_ERR_INVALID_ARG = 1,   /* null pointer, bad size, h_q % h_kv != 0, window without causal, non-finite scale */
+    ATTN_ERR_INVALID_ARG = 1,   /* null pointer, bad size, h_q % h_kv != 0, window without causal, scale not finite and > 0 */
     ATTN_ERR_UNSUPPORTED = 2,   /* a head size / dtype / head count with no kernel instantiated */
     ATTN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than *_workspace_size() */
     ATTN_ERR_HIP = 4            /* the HIP runtime rejected a launch */

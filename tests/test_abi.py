@@ -69,6 +69,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, window=8, causal=0) == 1   # window needs causal
     assert _prefill(lib, scale=float("nan")) == 1
     assert _prefill(lib, scale=float("inf")) == 1
+    assert _prefill(lib, scale=0.0) == 1
+    assert _prefill(lib, scale=-0.5) == 1
     assert _prefill(lib, d=64) == 2                 # bf16 kernel is d = 128
     assert _prefill(lib, dtype=0, d=48) == 2        # fp32 d not instantiated
     assert _prefill(lib, dtype=7) == 2
@@ -103,6 +105,7 @@ def test_mla_validation(lib):
                               a["dc"], a["dr"], a["scale"], a["split"], a["ws"], a["wsb"], None)
     assert mla(c=None) == 1
     assert mla(scale=float("nan")) == 1
+    assert mla(scale=0.0) == 1
     assert mla(split=32) == 1
     assert mla(dc=256) == 2
     assert mla(H=24) == 2

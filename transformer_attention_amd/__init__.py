@@ -23,7 +23,9 @@ import os
 import torch
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG_DIR, "libmi355attn.so")
+# MI355ATTN_LIB may point at another build of the same library (e.g. a
+# differently tuned one); by default the in-tree build is used.
+LIB_PATH = os.environ.get("MI355ATTN_LIB") or os.path.join(_PKG_DIR, "libmi355attn.so")
 
 ATTN_OK = 0
 ATTN_ERR_INVALID_ARG = 1

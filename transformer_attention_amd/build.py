@@ -11,6 +11,7 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(os.path.dirname(PKG_DIR), "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmi355attn.so")
 SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip",
            "mla_decode_bf16.hip"]
@@ -32,7 +33,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, extra_flags=None) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags or []) + srcs + ["-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE] + list(extra_flags or []) + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -5,7 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/mi355attn.h"
+#include "mi355attn.h"
 #include "kernels.h"
 
 namespace {
@@ -64,7 +64,7 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
     if (B <= 0 || T <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
     if (h_q % h_kv != 0) return ATTN_ERR_INVALID_ARG;
     if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_INVALID_ARG;
-    if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_INVALID_ARG;
     if ((long long)B * h_q * T * d_h >= (1LL << 40)) return ATTN_ERR_UNSUPPORTED;
     mi355::PrefillArgs a{q, k, v, o, lse, B, T, h_q, h_kv, d_h, causal ? 1 : 0, window, scale};
     hipError_t e;
@@ -101,7 +101,7 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     if (bad_ptr(q) || bad_ptr(k_cache) || bad_ptr(v_cache) || bad_ptr(o) || bad_ptr(seq_lens))
         return ATTN_ERR_INVALID_ARG;
     if (B <= 0 || S_max <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
-    if (h_q % h_kv != 0 || window < 0 || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+    if (h_q % h_kv != 0 || window < 0 || !isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_INVALID_ARG;
     if (split_tokens < 0 || split_tokens % 64) return ATTN_ERR_INVALID_ARG;
     if (d_h != 128) return ATTN_ERR_UNSUPPORTED;
     if (B > 65535 || h_kv * ((h_q / h_kv + 15) / 16) > 65535) return ATTN_ERR_UNSUPPORTED;
@@ -131,7 +131,8 @@ attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *ls
                          hipStream_t stream) {
     if (bad_ptr(q) || bad_ptr(kv_cache) || bad_ptr(o) || bad_ptr(seq_lens)) return ATTN_ERR_INVALID_ARG;
     if (B <= 0 || S_max <= 0 || h_q <= 0 || d_c <= 0 || d_r < 0) return ATTN_ERR_INVALID_ARG;
-    if (!isfinite(scale) || split_tokens < 0 || split_tokens % 64) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f) || split_tokens < 0 || split_tokens % 64)
+        return ATTN_ERR_INVALID_ARG;
     if (d_c != 512 || d_r != 64 || h_q % 16 != 0) return ATTN_ERR_UNSUPPORTED;
     if (B > 65535) return ATTN_ERR_UNSUPPORTED;
     const int split = split_tokens ? split_tokens : default_mla_split(B, S_max, h_q);

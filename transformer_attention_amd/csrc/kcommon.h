@@ -71,6 +71,44 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N & 0x30) << 10) | (0x7 << 4) | (0xF << 8));
 }
+// wait_vmcnt with a wave-uniform runtime count in [0, 31] (larger counts wait
+// for everything, which is always safe).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+    switch (n) {
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 9: wait_vmcnt<9>(); break;
+        case 10: wait_vmcnt<10>(); break;
+        case 11: wait_vmcnt<11>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        case 13: wait_vmcnt<13>(); break;
+        case 14: wait_vmcnt<14>(); break;
+        case 15: wait_vmcnt<15>(); break;
+        case 16: wait_vmcnt<16>(); break;
+        case 17: wait_vmcnt<17>(); break;
+        case 18: wait_vmcnt<18>(); break;
+        case 19: wait_vmcnt<19>(); break;
+        case 20: wait_vmcnt<20>(); break;
+        case 21: wait_vmcnt<21>(); break;
+        case 22: wait_vmcnt<22>(); break;
+        case 23: wait_vmcnt<23>(); break;
+        case 24: wait_vmcnt<24>(); break;
+        case 25: wait_vmcnt<25>(); break;
+        case 26: wait_vmcnt<26>(); break;
+        case 27: wait_vmcnt<27>(); break;
+        case 28: wait_vmcnt<28>(); break;
+        case 29: wait_vmcnt<29>(); break;
+        case 30: wait_vmcnt<30>(); break;
+        case 31: wait_vmcnt<31>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
+}
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // drain every outstanding global->LDS load); the asm statements keep the
 // compiler from moving memory accesses across it.  Callers order LDS

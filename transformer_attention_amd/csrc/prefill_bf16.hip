@@ -13,9 +13,10 @@
 // section 2, the zero-copy grouped broadcast instead of repeat_interleave).
 //
 // gfx950 mapping (the pages' kernels target A100/H100 and are prior art only):
-//  * workgroup = 8 waves, two per SIMD, so one wave's softmax (VALU, exp)
-//    overlaps the other's MFMAs; each wave owns 32 query rows of one query
-//    head; the workgroup covers 1, 2, 4 or 8 heads of the same K/V group;
+//  * workgroup = 256 query rows of 1, 2, 4 or 8 heads of one K/V group,
+//    as 8 waves of 32 rows (two waves per SIMD, one wave's softmax overlaps
+//    the other's MFMAs) or 4 waves of 64 rows (every K/V operand read from
+//    LDS feeds two MFMAs, halving LDS traffic per FLOP);
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //    (A = K rows from LDS, B = the wave's Q rows held in registers).  In the
 //    D layout each lane owns ONE query row (its column), so a row's max/sum
@@ -25,14 +26,20 @@
 //    the V^T A operand is read from the row-major V tile with the
 //    transposing LDS load ds_read_b64_tr_b16 (two per operand), whose four
 //    source rows are exactly the four keys each lane's P values belong to;
-//  * K and V tiles (64 keys) are stored row-major in LDS with a 304-byte row
-//    stride (19 16-byte slots, 19 = 3 mod 16): 16 consecutive rows of one
-//    column land in 16 distinct bank slots (conflict-free 16-byte K reads)
-//    and 4 consecutive rows x 32 bytes in 8 distinct slots (conflict-free
-//    transposing V reads), while every LDS address stays base + immediate;
-//  * tiles are double-buffered in LDS and staged through two register sets,
-//    so the global loads of tile t+2 are in flight while tile t is consumed
-//    (one barrier per tile);
+//  * K and V tiles (64 keys) are stored row-major in LDS with padded rows so
+//    every LDS address stays base + immediate and reads are bank-conflict
+//    free: K rows are 304 bytes apart (19 16-byte slots, 19 = 3 mod 16, so 16
+//    consecutive rows of one column hit 16 distinct slots), V rows 320 bytes
+//    apart (20 = 4 mod 16, so the 4 rows x 64 bytes a 32-lane half-wave
+//    reads through the transposing load hit 16 distinct slots);
+//  * K/V tiles stream HBM -> LDS through a 4-stage ring filled by
+//    global_load_lds_dwordx4 (no staging registers): while a wave computes
+//    the scores of tile t+1 and the P.V product of tile t, tiles t+2 and t+3
+//    are in flight (one barrier per tile);
+//  * each wave is software-pipelined: the MFMAs of the scores of tile t+1
+//    are issued between the exp/sum/convert of the probabilities of tile t,
+//    and the row max of tile t+1 is taken after the P.V MFMAs of tile t, so
+//    the matrix cores and the vector ALUs of one wave work concurrently;
 //  * the reference max is only moved when a tile's row max exceeds it by
 //    more than 2^8 (exact: every exponent is taken against the same
 //    reference max that l and O carry), so the O rescale is rare;
@@ -48,12 +55,10 @@ namespace mi355 {
 namespace {
 
 constexpr int D = 128;          // head size
-constexpr int BN = 64;          // keys per tile
-constexpr int NW = 8;           // waves per workgroup
-constexpr int RW = 32;          // query rows per wave
-constexpr int ROWB = D * 2 + 48;   // LDS row stride of a K/V row (304 B)
-constexpr int TILE_BYTES = BN * ROWB;          // 19456 B
-constexpr int LDS_BYTES = 4 * TILE_BYTES;      // K[2], V[2]
+constexpr int ROWB = D * 2 + 48;   // LDS row stride of a K row (304 B = 19 slots)
+constexpr int VROWB = D * 2 + 48;  // LDS row stride of a V row
+constexpr int LDS_BUDGET = 160 * 1024;
+constexpr int WG_ROWS = 256;    // query rows x heads per workgroup
 constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 
 struct Params {
@@ -62,21 +67,27 @@ struct Params {
     float *lse;
     int T, hq, hkv, G;
     int hpw;              // query heads per workgroup (1, 2, 4 or 8)
-    int rows_per_wg;      // RW * NW / hpw
+    int rows_per_wg;      // WG_ROWS / hpw
     int n_row_blocks;
     int n_head_groups;    // B * hkv * (G / hpw)
     int causal, window;
     float scale_log2;     // scale * log2(e)
 };
 
-// byte offset of (row, 16-byte chunk) inside a tile
+// byte offset of (row, 16-byte chunk) inside a K tile / a V tile
 __device__ __forceinline__ int tile_off(int r, int chunk) { return r * ROWB + (chunk << 4); }
+__device__ __forceinline__ int vtile_off(int r, int chunk) { return r * VROWB + (chunk << 4); }
 
-__device__ __forceinline__ bf16x4 lds_tr16(const char *base, int byte_off) {
-    return lds_read_tr16(base + byte_off);
-}
-
-__global__ __launch_bounds__(512, 1) void prefill_bf16_d128_kernel(Params p) {
+// NB = number of 32-row MFMA blocks per wave (1: 8 waves, 2: 4 waves);
+// KB = number of 32-key blocks per tile; NSTAGE = depth of the LDS ring.
+template <int NB, int KB, int NSTAGE>
+__global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Params p) {
+    constexpr int NW = 8 / NB;      // waves per workgroup
+    constexpr int RW = 32 * NB;     // query rows per wave
+    constexpr int BN = 32 * KB;     // keys per tile
+    constexpr int KTILE_BYTES = BN * ROWB;
+    constexpr int STAGE_BYTES = (2 * BN * ROWB + 1023) / 1024 * 1024;   // K rows, V rows
+    constexpr int AHEAD = NSTAGE - 1;                                  // tiles issued ahead
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -93,7 +104,7 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_d128_kernel(Params p) {
     const int sub = hg % subs;
     const int g = (hg / subs) % p.hkv;
     const int b = hg / (subs * p.hkv);
-    const int wph = NW / p.hpw;                       // waves per head
+    const int wph = NW / p.hpw;                       // waves per head (hpw <= NW)
     const int h = g * p.G + sub * p.hpw + wave / wph;
     const int r0 = rb * p.rows_per_wg;
     const int rw0 = r0 + (wave % wph) * RW;
@@ -107,189 +118,310 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_d128_kernel(Params p) {
     const bool wave_active = rw0 < T;
     const int kend_w = p.causal ? min(T, rw0 + RW) : T;
     const int kbeg_w = p.window > 0 ? max(0, rw0 - p.window + 1) : 0;
+    auto tile_active = [&](int t) {
+        const int ts = t * BN;
+        return wave_active && t < t_end && ts < kend_w && ts + BN > kbeg_w;
+    };
+    auto tile_needs_mask = [&](int t) {
+        const int ts = t * BN;
+        return (ts + BN > T) || (p.causal && ts + BN - 1 > rw0) ||
+               (p.window > 0 && (rw0 + RW - 1) - ts >= p.window);
+    };
 
     const size_t kv_base = ((size_t)b * p.hkv + g) * (size_t)T * D;
     const __bf16 *kg = p.k + kv_base;
     const __bf16 *vg = p.v + kv_base;
     const size_t q_base = ((size_t)b * p.hq + h) * (size_t)T * D;
-    const int row = rw0 + l32;                        // this lane's query row
+    const int row0 = rw0 + l32;                       // this lane's rows: row0 + 32 nb
+    const float c = p.scale_log2;
 
-    // Q^T B operands: row = rw0 + l32, d = 16ks + 8hi .. +7
-    bf16x8 qop[8];
+    // Q^T B operands: row = row0 + 32nb, d = 16ks + 8hi .. +7
+    bf16x8 qop[NB][8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (row < T) val = ldg16(p.q + q_base + (size_t)row * D + 16 * ks + 8 * hi);
-        qop[ks] = __builtin_bit_cast(bf16x8, val);
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int row = row0 + 32 * nb;
+            u32x4 val = {0u, 0u, 0u, 0u};
+            if (row < T) val = ldg16(p.q + q_base + (size_t)row * D + 16 * ks + 8 * hi);
+            qop[nb][ks] = __builtin_bit_cast(bf16x8, val);
+        }
+
+    f32x16 oacc[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[nb][db][i] = 0.f;
+    float m_run[NB], l_run[NB], mx_cur[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        m_run[nb] = -INFINITY;                        // reference max (log2 units)
+        l_run[nb] = 0.f;                              // lane-partial row sum
+        mx_cur[nb] = -INFINITY;                       // scaled max of the pending tile
     }
 
-    f32x16 oacc[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-
-    // Global -> register staging: K and V tiles are 64 rows x 16 chunks
-    // (1024 chunks each); thread handles chunks tid and tid + 512 of both.
-    // Two register sets: set (t & 1) holds tile t from its load until its store.
-    u32x4 kreg[2][2], vreg[2][2];
-    auto load_tile = [&](int t, int set) {
+    // LDS ring of NSTAGE stages, each holding the K and V rows of one tile.
+    // Tile t lives in stage (t - t_begin) % NSTAGE; at iteration t the stages
+    // hold tile t (V in use), t+1 (K in use), t+2 and t+3 (in flight).
+    auto kbuf = [&](int rel) { return smem + (rel % NSTAGE) * STAGE_BYTES; };
+    auto vbuf = [&](int rel) { return smem + (rel % NSTAGE) * STAGE_BYTES + KTILE_BYTES; };
+    // DMA of one tile: one-KB blocks (K rows, then V rows), split over the waves.
+    // LDS byte o of a region holds row o / stride, chunk (o % stride) / 16;
+    // pad slots receive an arbitrary valid chunk; rows past T re-read row T-1
+    // (their scores are masked, their P is 0).
+    constexpr int NBLK = STAGE_BYTES / 1024;
+    constexpr int PER_WAVE = (NBLK + NW - 1) / NW;
+    const int my_blk0 = PER_WAVE * wave;
+    const int my_nblk = min(PER_WAVE, NBLK - PER_WAVE * wave);
+    auto issue_tile = [&](int t) {
+        char *stage = smem + ((t - t_begin) % NSTAGE) * STAGE_BYTES;
         const int ts = t * BN;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 512 * i;
-            const int r = c >> 4, ch = c & 15;
-            const int key = ts + r;
-            u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (key < T) {
-                kv = ldg16(kg + (size_t)key * D + 8 * ch);
-                vv = ldg16(vg + (size_t)key * D + 8 * ch);
-            }
-            kreg[set][i] = kv;
-            vreg[set][i] = vv;
+        for (int i = 0; i < PER_WAVE; ++i) {
+            if (i >= my_nblk) break;
+            const int blk = my_blk0 + i;
+            const int o = blk * 1024 + lane * 16;
+            const bool is_v = o >= KTILE_BYTES;
+            const int ro = is_v ? o - KTILE_BYTES : o;
+            const int r = min(is_v ? ro / VROWB : ro / ROWB, BN - 1);   // constant divisors
+            const int ch = min((ro - r * (is_v ? VROWB : ROWB)) >> 4, D / 8 - 1);
+            const int key = min(ts + r, T - 1);
+            dma16((is_v ? vg : kg) + (size_t)key * D + 8 * ch, stage + blk * 1024);
         }
     };
-    auto store_tile = [&](int buf, int set) {
-        char *kt = smem + buf * TILE_BYTES;
-        char *vt = smem + (2 + buf) * TILE_BYTES;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 512 * i;
-            const int r = c >> 4, ch = c & 15;
-            *reinterpret_cast<u32x4 *>(kt + tile_off(r, ch)) = kreg[set][i];
-            *reinterpret_cast<u32x4 *>(vt + tile_off(r, ch)) = vreg[set][i];
-        }
+    auto wait_tiles = [&](int newer) {       // all but the `newer` most recent tiles landed
+        wait_vmcnt_dyn(newer <= 0 ? 0 : newer * my_nblk);
     };
 
-    // Per-lane constant parts of the LDS addresses.
-    // K operand (kb, ks): row 32kb + l32, chunk 2ks + hi.
-    // V operand (db, kb, half, e4): rows 32kb + 16half + 8e4 + 4hi + (j16>>2),
-    //   chunk 4db + 2(q16&1) + ((j16&3)>>1), byte 8*(j16&1).
+    // S^T = K Q^T for one tile: s[nb][kb] holds keys 32kb + 8(i/4) + 4hi + (i%4)
+    // of row row0 + 32nb.
+    auto qk = [&](const char *kt, f32x16 (&s)[NB][KB]) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[nb][kb][i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + tile_off(32 * kb + l32, 2 * ks + hi));
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) s[nb][kb] = mfma32x32x16(a, qop[nb][ks], s[nb][kb]);
+            }
+    };
+    // Mask tile t in place (raw scores -> -inf where the key is not visible).
+    // Element (kb, i) is key ts + 4hi + e with e = 32kb + 8(i/4) + (i%4).
+    auto apply_mask = [&](int t, f32x16 (&s)[NB][KB]) {
+        const int base = t * BN + 4 * hi;
+        const int lim_t = T - base;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int diff = row0 + 32 * nb - base;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int e = 32 * kb + 8 * (i >> 2) + (i & 3);
+                    bool vis = e < lim_t;
+                    if (p.causal) vis = vis && e <= diff;
+                    if (p.window > 0) vis = vis && diff - e < p.window;
+                    s[nb][kb][i] = vis ? s[nb][kb][i] : -INFINITY;
+                }
+        }
+    };
+    // Row max of a (masked) tile in log2 units; scale > 0 so max(c s) = c max(s).
+    auto tile_max = [&](const f32x16 (&s)[KB]) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        return mx * c;
+    };
+    // V^T operand for (db, kb, half): two transposing reads of rows
+    // 32kb + 16half + 4hi + (j16>>2) (+8), d = 32db + 16(q16&1) + 4(j16&3) .. +3.
     const int v_row_lane = 4 * hi + (j16 >> 2);
     const int v_chunk_lane = 2 * (q16 & 1) + ((j16 & 3) >> 1);
     const int v_byte_lane = 8 * (j16 & 1);
-
-    if (t_begin < t_end) load_tile(t_begin, 0);
-    if (t_begin + 1 < t_end) load_tile(t_begin + 1, 1);
-
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        // register set `buf` holds tile t; after the store it takes tile t+2
-        if (buf == 0) store_tile(0, 0); else store_tile(1, 1);
-        __syncthreads();
-        if (t + 2 < t_end) { if (buf == 0) load_tile(t + 2, 0); else load_tile(t + 2, 1); }
-
-        const int ts = t * BN;
-        const bool do_tile = wave_active && ts < kend_w && ts + BN > kbeg_w;
-        if (!do_tile) continue;
-        const char *kt = smem + buf * TILE_BYTES;
-        const char *vt = smem + (2 + buf) * TILE_BYTES;
-
-        // S^T = K Q^T : sacc[kb], 32 keys x 32 rows each.
-        f32x16 sacc[2];
+    auto v_operand = [&](const char *vt, int db, int kb, int half) {
+        const int rA = 32 * kb + 16 * half + v_row_lane;
+        const int ch = 4 * db + v_chunk_lane;
+        const bf16x4 lo4 = lds_read_tr16(vt + vtile_off(rA, ch) + v_byte_lane);
+        const bf16x4 hi4 = lds_read_tr16(vt + vtile_off(rA + 8, ch) + v_byte_lane);
+        return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // Probabilities of key block kb (16 values) -> two bf16x8 B operands; adds to lsum.
+    auto probs = [&](const f32x16 &s, float m_use, float &lsum, bf16x8 &p0, bf16x8 &p1) {
+        float pv[16];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int r = 32 * kb + l32;
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + tile_off(r, 2 * ks + hi));
-                sacc[kb] = mfma32x32x16(a, qop[ks], sacc[kb]);
-            }
+        for (int i = 0; i < 16; ++i) {
+            pv[i] = fast_exp2(__builtin_fmaf(s[i], c, -m_use));
+            lsum += pv[i];
         }
+        p0 = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        p1 = to_bf16x8(pv[8], pv[9], pv[10], pv[11], pv[12], pv[13], pv[14], pv[15]);
+    };
 
-        const bool need_mask =
-            (ts + BN > T) ||
-            (p.causal && ts + BN - 1 > rw0) ||
-            (p.window > 0 && (rw0 + RW - 1) - ts >= p.window);
-        float mx = -INFINITY;
+    // ---- prologue: tiles tb .. tb+AHEAD-1 in flight; S(tb) and its max ----
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float v = sacc[kb][i] * p.scale_log2;
-                if (need_mask) {
-                    const int key = ts + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    bool vis = key < T;
-                    if (p.causal) vis = vis && key <= row;
-                    if (p.window > 0) vis = vis && (row - key) < p.window;
-                    v = vis ? v : -INFINITY;
-                }
-                sacc[kb][i] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const bool upd = mx > m_run + TAU;
-        const float m_new = upd ? mx : m_run;
-        const float alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
-        m_run = m_new;
-        if (__any(upd)) {
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        }
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        float lsum = 0.f;
-        bf16x8 pop[2][2];   // [kb][half]
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            float pv[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                pv[i] = fast_exp2(sacc[kb][i] - m_use);
-                lsum += pv[i];
-            }
-            pop[kb][0] = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-            pop[kb][1] = to_bf16x8(pv[8], pv[9], pv[10], pv[11], pv[12], pv[13], pv[14], pv[15]);
-        }
-        l_run = l_run * alpha + lsum;
+    for (int i = 0; i < AHEAD; ++i)
+        if (t_begin + i < t_end) issue_tile(t_begin + i);
+    wait_tiles(min(AHEAD - 1, t_end - t_begin - 1));  // tile tb landed (q loads are older)
+    raw_barrier();
 
-        // O^T += V^T P^T
+    f32x16 sa[NB][KB], sb[NB][KB];
+    if (tile_active(t_begin)) {
+        qk(kbuf(0), sa);
+        if (tile_needs_mask(t_begin)) apply_mask(t_begin, sa);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-#pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    const int rA = 32 * kb + 16 * half + v_row_lane;
-                    const int ch = 4 * db + v_chunk_lane;
-                    const bf16x4 lo4 = lds_tr16(vt, tile_off(rA, ch) + v_byte_lane);
-                    const bf16x4 hi4 = lds_tr16(vt, tile_off(rA + 8, ch) + v_byte_lane);
-                    const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                    oacc[db] = mfma32x32x16(a, pop[kb][half], oacc[db]);
-                }
+        for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = tile_max(sa[nb]);
     }
+
+    // One iteration: softmax + P.V of tile t (scores in s_cur), scores of
+    // tile t+1 into s_nxt.
+    auto iteration = [&](int t, f32x16 (&s_cur)[NB][KB], f32x16 (&s_nxt)[NB][KB]) {
+        const int rel = t - t_begin;
+        wait_tiles(min(AHEAD - 2, t_end - t - 2));    // tile t+1 landed
+        raw_barrier();                                // iteration t-1 done everywhere
+        if (t + AHEAD < t_end) issue_tile(t + AHEAD); // into the stage of tile t-1
+
+        const bool act_c = tile_active(t);
+        const bool act_n = tile_active(t + 1);
+        const char *kn = kbuf(rel + 1);
+        const char *vc = vbuf(rel);
+
+        float m_use[NB];
+        if (act_c) {
+            bool any_upd = false;
+            float alpha[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const bool upd = mx_cur[nb] > m_run[nb] + TAU;
+                const float m_new = upd ? mx_cur[nb] : m_run[nb];
+                alpha[nb] = upd ? fast_exp2(m_run[nb] - m_new) : 1.0f;
+                any_upd = any_upd || __any(upd);
+                l_run[nb] *= alpha[nb];
+                m_run[nb] = m_new;
+                m_use[nb] = (m_new == -INFINITY) ? 0.f : m_new;
+            }
+            if (any_upd) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) oacc[nb][db] *= alpha[nb];
+            }
+        }
+
+        if (act_c) {
+            // scores of tile t+1 interleaved with the probabilities of tile t
+            // (when t+1 is not this wave's, the scores are computed and dropped:
+            // the stage holds valid LDS data and s_nxt is not used)
+            float lsum[NB];
+            bf16x8 pop[NB][KB][2];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                lsum[nb] = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s_nxt[nb][kb][i] = 0.f;
+            }
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kn + tile_off(32 * kb + l32, 2 * ks + hi));
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) s_nxt[nb][kb] = mfma32x32x16(a, qop[nb][ks], s_nxt[nb][kb]);
+                }
+                // spread the NB*KB probability blocks over the 8 MFMA steps
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+                        if (ks == 1 + (6 * (nb * KB + kb)) / (NB * KB))
+                            probs(s_cur[nb][kb], m_use[nb], lsum[nb], pop[nb][kb][0], pop[nb][kb][1]);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) l_run[nb] += lsum[nb];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) {
+                        const bf16x8 a = v_operand(vc, db, kb, half);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            oacc[nb][db] = mfma32x32x16(a, pop[nb][kb][half], oacc[nb][db]);
+                    }
+        } else if (act_n) {
+            qk(kn, s_nxt);
+        }
+        if (act_n) {
+            if (tile_needs_mask(t + 1)) apply_mask(t + 1, s_nxt);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = tile_max(s_nxt[nb]);
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = -INFINITY;
+        }
+    };
+
+    int t = t_begin;
+    for (; t + 1 < t_end; t += 2) {
+        iteration(t, sa, sb);
+        iteration(t + 1, sb, sa);
+    }
+    if (t < t_end) iteration(t, sa, sb);
 
     if (!wave_active) return;
     // Epilogue: O = O~ / l, L = m ln2 + ln l.
-    const float lt = l_run + shfl_xor(l_run, 32);
-    if (row >= T) return;
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    __bf16 *orow = p.o + q_base + (size_t)row * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int nb = 0; nb < NB; ++nb) {
+        const int row = row0 + 32 * nb;
+        const float lt = l_run[nb] + shfl_xor(l_run[nb], 32);
+        if (row >= T) continue;
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        __bf16 *orow = p.o + q_base + (size_t)row * D;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int d = 32 * db + 8 * q4 + 4 * hi;
-            u32x2 w = {pack_bf16x2(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv),
-                       pack_bf16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv)};
-            *reinterpret_cast<u32x2 *>(orow + d) = w;
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = 32 * db + 8 * q4 + 4 * hi;
+                u32x2 w = {pack_bf16x2(oacc[nb][db][4 * q4 + 0] * inv, oacc[nb][db][4 * q4 + 1] * inv),
+                           pack_bf16x2(oacc[nb][db][4 * q4 + 2] * inv, oacc[nb][db][4 * q4 + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(orow + d) = w;
+            }
+        if (p.lse && hi == 0) {
+            const size_t li = ((size_t)b * p.hq + h) * (size_t)T + row;
+            p.lse[li] = lt > 0.f ? m_run[nb] * kLn2 + __logf(lt) : -INFINITY;
         }
-    if (p.lse && hi == 0) {
-        const size_t li = ((size_t)b * p.hq + h) * (size_t)T + row;
-        p.lse[li] = lt > 0.f ? m_run * kLn2 + __logf(lt) : -INFINITY;
     }
 }
+
+#ifndef PREFILL_NB
+#define PREFILL_NB 1
+#endif
+#ifndef PREFILL_KB
+#define PREFILL_KB 2
+#endif
+#ifndef PREFILL_NSTAGE
+#define PREFILL_NSTAGE 4
+#endif
 
 }  // namespace
 
 hipError_t launch_prefill_bf16_d128(const PrefillArgs &a, hipStream_t stream) {
+    constexpr int NB = PREFILL_NB, KB = PREFILL_KB, NST = PREFILL_NSTAGE;
+    constexpr int NW = 8 / NB;
+    constexpr int LDS_BYTES = NST * ((2 * 32 * KB * ROWB + 1023) / 1024 * 1024);
+    static_assert(LDS_BYTES <= LDS_BUDGET, "LDS ring too large");
     Params p;
     p.q = static_cast<const __bf16 *>(a.q);
     p.k = static_cast<const __bf16 *>(a.k);
@@ -300,8 +432,9 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs &a, hipStream_t stream) {
     p.hq = a.hq;
     p.hkv = a.hkv;
     p.G = a.hq / a.hkv;
-    p.hpw = (p.G % 8 == 0) ? 8 : (p.G % 4 == 0) ? 4 : (p.G % 2 == 0 ? 2 : 1);
-    p.rows_per_wg = RW * NW / p.hpw;
+    const int hmax = NW;                      // at most one head per wave
+    p.hpw = (p.G % 8 == 0 && hmax >= 8) ? 8 : (p.G % 4 == 0) ? 4 : (p.G % 2 == 0 ? 2 : 1);
+    p.rows_per_wg = WG_ROWS / p.hpw;
     p.n_row_blocks = (a.T + p.rows_per_wg - 1) / p.rows_per_wg;
     p.n_head_groups = a.B * a.hkv * (p.G / p.hpw);
     p.causal = a.causal;
@@ -309,15 +442,15 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs &a, hipStream_t stream) {
     p.scale_log2 = a.scale * kLog2e;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)prefill_bf16_d128_kernel,
+        hipError_t e = hipFuncSetAttribute((const void *)prefill_bf16_d128_kernel<NB, KB, NST>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const long long nblocks = (long long)p.n_row_blocks * p.n_head_groups;
     if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(prefill_bf16_d128_kernel, dim3((unsigned)nblocks), dim3(64 * NW), LDS_BYTES,
-                       stream, p);
+    hipLaunchKernelGGL((prefill_bf16_d128_kernel<NB, KB, NST>), dim3((unsigned)nblocks), dim3(64 * NW),
+                       LDS_BYTES, stream, p);
     return hipGetLastError();
 }
 
