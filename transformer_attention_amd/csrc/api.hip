@@ -15,7 +15,7 @@ namespace {
 // per CU for full-length sequences while each one still streams many tiles.
 int default_decode_split(int B, int S_max, int hkv, int G) {
     const long long groups = (long long)B * hkv * ((G + 15) / 16);
-    int split = 4096;
+    int split = 8192;
     while (split > 256 && groups * ((S_max + split - 1) / split) < 2048) split /= 2;
     return split;
 }

@@ -15,21 +15,24 @@
 // The cache of each (sequence, K/V head) is cut into chunks of `split` keys;
 // one workgroup handles one chunk for up to 16 query heads of the group, so
 // every K/V byte of the chunk is read from HBM once:
-//  * 64-key tiles of K and V stream HBM -> LDS through a 4-stage ring filled
-//    by global_load_lds_dwordx4 (three tiles in flight per CU, no staging
-//    registers); rows are stored with a 304-byte stride (19 = 3 mod 16 bank
-//    slots), so 16-byte reads down a column and transposing reads of 4 rows
-//    are bank-conflict free and all addresses are base + immediate;
-//  * each of the 4 waves computes the whole score tile S^T = K q^T
-//    (v_mfma_f32_16x16x32_bf16, the group's heads as the 16 columns) and the
-//    softmax -- MFMA time is small next to the tile's HBM time, and doing it
-//    redundantly gives every wave the same (m, l) with no exchange -- then
-//    the P.V product for its own quarter of d: O^T = V^T P^T, with V^T read
-//    by ds_read_b64_tr_b16 and the rounded probabilities as the B operand;
-//  * the chunk's normalised partial output and log-sum-exp go to the
-//    workspace; a second kernel merges the chunks of each (sequence, head):
-//    L = log sum_s exp(L_s), O = sum_s exp(L_s - L) O_s, the FlashAttention-2
-//    state merge ("Attention Engineering ...", section 4).
+//  * the chunk's 32-key tiles are dealt round-robin to the 4 waves; each wave
+//    streams its tiles HBM -> LDS through a private 2-stage ring filled by
+//    global_load_lds_dwordx4 (no staging registers, no workgroup barrier in
+//    the loop: a wave waits only for its own copies);
+//  * K rows are stored 272 bytes apart (17 16-byte slots: 16 consecutive rows
+//    of one column hit 16 distinct bank slots) and V rows 288 bytes apart
+//    (18 = 2 mod 16: the 8 rows x 32 bytes a half-wave reads through the
+//    transposing load hit 16 distinct slots), so all LDS reads are
+//    conflict-free and every address is base + immediate;
+//  * per tile: S^T = K q^T with v_mfma_f32_16x16x32_bf16 (the group's heads are
+//    the 16 columns), online softmax per head column, then O^T = V^T P^T with
+//    V^T read by ds_read_b64_tr_b16 and the rounded probabilities as the B
+//    operand;
+//  * the four waves' (m, l, O) are merged through LDS, and the chunk's
+//    normalised partial output and log-sum-exp go to the workspace; a second
+//    kernel merges the chunks of each (sequence, head): L = log sum_s exp(L_s),
+//    O = sum_s exp(L_s - L) O_s, the FlashAttention-2 state merge
+//    ("Attention Engineering ...", section 4).
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -37,13 +40,15 @@ namespace mi355 {
 namespace {
 
 constexpr int D = 128;
-constexpr int BN = 64;                    // keys per tile
+constexpr int BN = 32;                    // keys per tile
 constexpr int NW = 4;                     // waves per workgroup
-constexpr int LROW = D * 2 + 48;          // LDS row stride, bytes (304)
-constexpr int REGION = BN * LROW;         // 19456 B: K rows, then V rows
-constexpr int TILE_BYTES = 2 * REGION;    // 38912 B = 38 one-KB DMA blocks
-constexpr int NSTAGE = 4;
-constexpr int LDS_BYTES = NSTAGE * TILE_BYTES;   // 155648
+constexpr int KROW = D * 2 + 16;          // 272 B
+constexpr int VROW = D * 2 + 32;          // 288 B
+constexpr int KREG = BN * KROW;           // 8704 B
+constexpr int STAGE_BLK = (BN * (KROW + VROW) + 1023) / 1024;   // 18 one-KB blocks
+constexpr int STAGE_BYTES = STAGE_BLK * 1024;                   // 18432 B
+constexpr int WAVE_BYTES = 2 * STAGE_BYTES;                     // private ring
+constexpr int LDS_BYTES = NW * WAVE_BYTES;                      // 147456 B
 constexpr float TAU = 8.0f;
 
 struct Params {
@@ -54,8 +59,6 @@ struct Params {
     int split, n_split_max, window;
     float scale_log2;
 };
-
-__device__ __forceinline__ int tile_off(int r, int chunk) { return r * LROW + (chunk << 4); }
 
 __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -76,6 +79,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
     const int lo = max(s * p.split, kvis);
     const int hi = min((s + 1) * p.split, len);
     const int n_tiles = lo < hi ? (hi - lo + BN - 1) / BN : 0;
+    // this wave's tiles: w, w + NW, ...
+    const int my_tiles = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
 
     const int hidx = hc * 16 + j16;                       // head within the group (column)
     const bool head_ok = hidx < p.G;
@@ -83,33 +88,40 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
     const size_t kv_base = ((size_t)b * p.hkv + g) * (size_t)p.S_max * D;
     const char *kg = reinterpret_cast<const char *>(p.k + kv_base);
     const char *vg = reinterpret_cast<const char *>(p.v + kv_base);
+    char *ring = smem + wave * WAVE_BYTES;
 
-    // DMA of tile t: blocks 0-18 fill the K rows, 19-37 the V rows; waves 0-1
-    // issue 10 blocks, waves 2-3 issue 9.  LDS byte o of a region holds row
-    // o / 304, chunk (o % 304) / 16; pad slots receive an arbitrary valid
-    // chunk, rows past the chunk end re-read the last valid key (masked).
-    const int my_blk0 = wave < 2 ? 10 * wave : 20 + 9 * (wave - 2);
-    const int my_nblk = wave < 2 ? 10 : 9;
-    auto issue_tile = [&](int t) {
-        char *stage = smem + (t % NSTAGE) * TILE_BYTES;
-        const int t0 = lo + t * BN;
+    // Per-lane DMA sources, relative to the tile's first key: block i of a
+    // stage covers stage bytes [1024 i, 1024 i + 1024); lane byte o = 1024 i +
+    // 16 lane holds K row o / 272 (o < 8704) or V row (o - 8704) / 288, chunk
+    // (remainder) / 16 (pad slots and bytes past the last row take a valid
+    // chunk of the last row).  rel_row[i] is that row, src[i] the row-0 address.
+    int rel_row[STAGE_BLK];
+    const char *src[STAGE_BLK];
 #pragma unroll
-        for (int i = 0; i < 10; ++i) {
-            if (i >= my_nblk) break;
-            const int blk = my_blk0 + i;
-            const int o = blk * 1024 + lane * 16;
-            const bool is_v = o >= REGION;
-            const int ro = is_v ? o - REGION : o;
-            const int r = ro / LROW;
-            const int ch = min((ro - r * LROW) >> 4, D / 8 - 1);
-            const int key = min(t0 + r, hi - 1);
-            const char *src = (is_v ? vg : kg) + (size_t)key * (D * 2) + ch * 16;
-            dma16(src, stage + blk * 1024);
+    for (int i = 0; i < STAGE_BLK; ++i) {
+        const int o = i * 1024 + lane * 16;
+        const bool is_v = o >= KREG;
+        const int ro = is_v ? o - KREG : o;
+        const int r = min(is_v ? ro / VROW : ro / KROW, BN - 1);
+        const int ch = min((ro - r * (is_v ? VROW : KROW)) >> 4, D / 8 - 1);
+        rel_row[i] = r;
+        src[i] = (is_v ? vg : kg) + ch * 16;
+    }
+    auto issue = [&](int j) {                             // j-th tile of this wave
+        const int t0 = lo + (wave + NW * j) * BN;
+        char *stage = ring + (j & 1) * STAGE_BYTES;
+        if (t0 + BN <= hi) {
+#pragma unroll
+            for (int i = 0; i < STAGE_BLK; ++i)
+                dma16(src[i] + (size_t)(t0 + rel_row[i]) * (D * 2), stage + i * 1024);
+        } else {
+#pragma unroll
+            for (int i = 0; i < STAGE_BLK; ++i)
+                dma16(src[i] + (size_t)min(t0 + rel_row[i], hi - 1) * (D * 2), stage + i * 1024);
         }
     };
-#pragma unroll
-    for (int t = 0; t < NSTAGE - 1; ++t)
-        if (t < n_tiles) issue_tile(t);
+    if (my_tiles > 0) issue(0);
+    if (my_tiles > 1) issue(1);
 
     // q^T as B operand: column = head j16, d = 32ks + 8 q16 .. +7.
     bf16x8 qop[4];
@@ -120,42 +132,36 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         qop[ks] = __builtin_bit_cast(bf16x8, val);
     }
 
-    f32x4 oacc[2];                                        // d = 32 wave + 16 dbl + 4 q16 + i
-    oacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    oacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-    const int v_row_lane = 4 * q16 + (j16 >> 2);
-    const int v_chunk_lane = 4 * wave + ((j16 & 3) >> 1);  // chunk of d = 32 wave + 16 dbl + 4(j%4)
-    const int v_byte_lane = 8 * (j16 & 1);
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const int newer = t == 0 ? 0 : min(NSTAGE - 2, n_tiles - 1 - t);
-        if (newer == 0) wait_vmcnt<0>();
-        else if (newer == 1) { if (my_nblk == 10) wait_vmcnt<10>(); else wait_vmcnt<9>(); }
-        else { if (my_nblk == 10) wait_vmcnt<20>(); else wait_vmcnt<18>(); }
-        raw_barrier();
-        if (t + NSTAGE - 1 < n_tiles) issue_tile(t + NSTAGE - 1);
-
-        const char *kt = smem + (t % NSTAGE) * TILE_BYTES;
-        const char *vt = kt + REGION;
-        const int t0 = lo + t * BN;
-        // S^T blocks mb = 0..3: key 16mb + j16 (A row), element (mb, i) of this
-        // lane = key t0 + 16mb + 4 q16 + i of head column j16.
-        f32x4 sacc[4];
+    f32x4 oacc[8];                                        // d = 16 db + 4 q16 + i, head j16
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+    for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    // V^T operand: lane j of group q16 addresses V row 4 q16 + j/4 (second
+    // read: +16), d = 16 db + 4 (j%4) .. +3: chunk 2 db + (j%4)/2, byte 8 (j%2).
+    const int v_lane_off = KREG + (4 * q16 + (j16 >> 2)) * VROW + ((j16 & 3) >> 1) * 16 + 8 * (j16 & 1);
+    const int k_lane_off = j16 * KROW + q16 * 16;
+
+    for (int j = 0; j < my_tiles; ++j) {
+        // stage j&1 landed; tile j+1 (if any) may still be in flight
+        if (j + 1 < my_tiles) wait_vmcnt<STAGE_BLK>(); else wait_vmcnt<0>();
+        const char *st = ring + (j & 1) * STAGE_BYTES;
+        const int t0 = lo + (wave + NW * j) * BN;
+        f32x4 sacc[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
             sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + tile_off(16 * mb + j16, 4 * ks + q16));
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(st + k_lane_off + 16 * mb * KROW + 64 * ks);
                 sacc[mb] = mfma16x16x32(a, qop[ks], sacc[mb]);
             }
         }
+        // element (mb, i) of this lane is key t0 + 16 mb + 4 q16 + i of head column j16
         const bool tail = t0 + BN > hi;
-        float x[16];
+        float x[8];
         float mx = -INFINITY;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float v = sacc[mb][i] * p.scale_log2;
@@ -169,43 +175,80 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         const float m_new = upd ? mx : m_run;
         const float alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
         m_run = m_new;
-        oacc[0] *= alpha;
-        oacc[1] *= alpha;
+        if (__any(upd)) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+        }
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        float pv[16];
+        float pv[8];
         float lsum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int e = 0; e < 8; ++e) {
             pv[e] = fast_exp2(x[e] - m_use);
             lsum += pv[e];
         }
         l_run = l_run * alpha + lsum;
-        // K-step kk covers keys 32kk .. 32kk+31: elements (mb = 2kk, i) then (2kk+1, i)
+        const bf16x8 pop = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 pop = to_bf16x8(pv[8 * kk + 0], pv[8 * kk + 1], pv[8 * kk + 2], pv[8 * kk + 3],
-                                         pv[8 * kk + 4], pv[8 * kk + 5], pv[8 * kk + 6], pv[8 * kk + 7]);
-#pragma unroll
-            for (int dbl = 0; dbl < 2; ++dbl) {
-                const int r = 32 * kk + v_row_lane;
-                const int ch = v_chunk_lane + 2 * dbl;
-                const bf16x4 lo4 = lds_read_tr16(vt + tile_off(r, ch) + v_byte_lane);
-                const bf16x4 hi4 = lds_read_tr16(vt + tile_off(r + 16, ch) + v_byte_lane);
-                const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[dbl] = mfma16x16x32(a, pop, oacc[dbl]);
-            }
+        for (int db = 0; db < 8; ++db) {
+            const bf16x4 lo4 = lds_read_tr16(st + v_lane_off + 32 * db);
+            const bf16x4 hi4 = lds_read_tr16(st + v_lane_off + 16 * VROW + 32 * db);
+            const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[db] = mfma16x16x32(a, pop, oacc[db]);
+        }
+        // refill the stage with tile j+2 once every read of it has returned
+        if (j + 2 < my_tiles) {
+            asm volatile("" ::: "memory");
+            wait_lgkmcnt0();
+            issue(j + 2);
         }
     }
     float lt = l_run + shfl_xor(l_run, 16);
     lt += shfl_xor(lt, 32);
-    if (!head_ok) return;
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const size_t ws = ((size_t)b * p.hq + h) * p.n_split_max + s;
-    float *wo = p.ws_o + ws * D;
+
+    // Merge the four waves through LDS (reusing the rings).
+    wait_vmcnt<0>();
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(smem);        // [NW][16 heads][D] + m, l
+    float *red_m = red + NW * 16 * D;
+    float *red_l = red_m + NW * 16;
 #pragma unroll
-    for (int dbl = 0; dbl < 2; ++dbl)
-        *reinterpret_cast<f32x4 *>(wo + 32 * wave + 16 * dbl + 4 * q16) = oacc[dbl] * inv;
-    if (wave == 0 && q16 == 0) p.ws_lse[ws] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
+    for (int db = 0; db < 8; ++db)
+        *reinterpret_cast<f32x4 *>(red + (wave * 16 + j16) * D + 16 * db + 4 * q16) = oacc[db];
+    if (q16 == 0) {
+        red_m[wave * 16 + j16] = m_run;
+        red_l[wave * 16 + j16] = lt;
+    }
+    __syncthreads();
+    {
+        const int hh = tid >> 4;                          // 16 heads x 16 threads
+        const int d0 = (tid & 15) * 8;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w * 16 + hh]);
+        const float Mu = (M == -INFINITY) ? 0.f : M;
+        float L = 0.f, wgt[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            wgt[w] = fast_exp2(red_m[w * 16 + hh] - Mu);
+            L += wgt[w] * red_l[w * 16 + hh];
+        }
+        const float inv = L > 0.f ? 1.0f / L : 0.f;
+        const int hidx2 = hc * 16 + hh;
+        if (hidx2 < p.G) {
+            const int h2 = g * p.G + hidx2;
+            const size_t ws = (((size_t)b * p.hq + h2) * p.n_split_max + s);
+            float *wo = p.ws_o + ws * D;
+#pragma unroll
+            for (int dd = 0; dd < 8; ++dd) {
+                float acc = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) acc += wgt[w] * red[(w * 16 + hh) * D + d0 + dd];
+                wo[d0 + dd] = acc * inv;
+            }
+            if ((tid & 15) == 0) p.ws_lse[ws] = L > 0.f ? Mu + __log2f(L) : -INFINITY;
+        }
+    }
 }
 
 // One wave per (head, sequence): merge the partials of the sequence's splits.

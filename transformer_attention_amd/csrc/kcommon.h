@@ -109,12 +109,18 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
         default: wait_vmcnt<0>(); break;
     }
 }
+// s_waitcnt lgkmcnt(0): every LDS read this wave issued has returned.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
 // Workgroup barrier without the memory fence of __syncthreads (which would
-// drain every outstanding global->LDS load); the asm statements keep the
-// compiler from moving memory accesses across it.  Callers order LDS
-// accesses themselves with wait_vmcnt / the lgkmcnt waits the compiler emits.
+// drain every outstanding global->LDS load).  The wave's own LDS reads are
+// complete before it arrives (so a stage may be refilled by any wave after
+// the barrier), and the asm statements keep the compiler from moving memory
+// accesses across it.  Global->LDS copies are ordered with wait_vmcnt.
 __device__ __forceinline__ void raw_barrier() {
     asm volatile("" ::: "memory");
+    wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
