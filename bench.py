@@ -146,7 +146,7 @@ def cpu_baseline_prefill(W, shape, budget_s=20.0):
             break
         n_rows = min(shape.T, n_rows * 2)
     vis = 0
-    for r in rows:
+    for r in rows.tolist():
         lo = max(0, r - shape.window + 1) if shape.window else 0
         hi = r + 1 if shape.causal else shape.T
         vis += hi - lo

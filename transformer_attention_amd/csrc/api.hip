@@ -10,14 +10,18 @@
 
 namespace {
 
-// Default split of the cache for decode, in keys (a multiple of the 64-key
-// tile).  Each split is one workgroup; the choice keeps several workgroups
-// per CU for full-length sequences while each one still streams many tiles.
-int default_decode_split(int B, int S_max, int hkv, int G) {
+// Default split of the cache for decode, in keys (a multiple of the 32-key
+// tile).  A split is one unit of work of the persistent decode kernel; the
+// choice aims at about 8 units per wave (4 waves per CU) for full-length
+// sequences, which balances the waves while keeping units long.
+int device_cu_count();
+int default_decode_split(int B, int S_max, int hkv, int G, int num_cus) {
     const long long groups = (long long)B * hkv * ((G + 15) / 16);
-    int split = 8192;
-    while (split > 256 && groups * ((S_max + split - 1) / split) < 2048) split /= 2;
-    return split;
+    const long long target_units = 8LL * 4 * num_cus;
+    long long split = groups * (long long)S_max / target_units;
+    int p2 = 256;
+    while (p2 < 8192 && p2 < split) p2 *= 2;
+    return p2;
 }
 
 // MLA: one workgroup per (sequence, 128-head chunk, split); aim at one
@@ -38,6 +42,19 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 size_t split_ws_bytes(long long rows, long long n_split, long long dv) {
     return align_up((size_t)(rows * n_split * dv) * sizeof(float), 256) +
            align_up((size_t)(rows * n_split) * sizeof(float), 256);
+}
+
+// Compute units of the current device (cached per device id).
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < 64) cached[dev] = n;
+    return n;
 }
 
 }  // namespace
@@ -82,7 +99,7 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
 }
 
 static int resolve_decode_split(int split_tokens, int B, int S_max, int h_q, int h_kv) {
-    if (split_tokens == 0) return default_decode_split(B, S_max, h_kv, h_q / h_kv);
+    if (split_tokens == 0) return default_decode_split(B, S_max, h_kv, h_q / h_kv, device_cu_count());
     return split_tokens;
 }
 
@@ -91,7 +108,7 @@ size_t attn_decode_workspace_size(int B, int S_max, int h_q, int h_kv, int d_h, 
     if (split_tokens < 0 || split_tokens % 64) return 0;
     const int split = resolve_decode_split(split_tokens, B, S_max, h_q, h_kv);
     const long long ns = (S_max + split - 1) / split;
-    return split_ws_bytes((long long)B * h_q, ns, d_h);
+    return split_ws_bytes((long long)B * h_q, ns, d_h) + align_up((size_t)(B + 1) * sizeof(int32_t), 256);
 }
 
 attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *o,
@@ -110,10 +127,11 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     const size_t need = attn_decode_workspace_size(B, S_max, h_q, h_kv, d_h, split_tokens);
     if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     float *ws_o = static_cast<float *>(workspace);
-    float *ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                              align_up((size_t)B * h_q * ns * d_h * sizeof(float), 256));
+    char *ws_end = static_cast<char *>(workspace) + align_up((size_t)B * h_q * ns * d_h * sizeof(float), 256);
+    float *ws_lse = reinterpret_cast<float *>(ws_end);
+    int32_t *plan = reinterpret_cast<int32_t *>(ws_end + align_up((size_t)B * h_q * ns * sizeof(float), 256));
     mi355::DecodeArgs a{q, k_cache, v_cache, o, lse, seq_lens, B, S_max, h_q, h_kv, d_h,
-                        window, scale, split, ns, ws_o, ws_lse};
+                        window, scale, split, ns, ws_o, ws_lse, plan, device_cu_count()};
     return mi355::launch_decode_bf16_d128(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

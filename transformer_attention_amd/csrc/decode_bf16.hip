@@ -12,27 +12,28 @@
 // "Decoding Attention Arithmetic Intensity"), so the design goal is to read
 // each cached K/V byte exactly once, coalesced, with many bytes in flight.
 //
-// The cache of each (sequence, K/V head) is cut into chunks of `split` keys;
-// one workgroup handles one chunk for up to 16 query heads of the group, so
-// every K/V byte of the chunk is read from HBM once:
-//  * the chunk's 32-key tiles are dealt round-robin to the 4 waves; each wave
-//    streams its tiles HBM -> LDS through a private 2-stage ring filled by
-//    global_load_lds_dwordx4 (no staging registers, no workgroup barrier in
-//    the loop: a wave waits only for its own copies);
+// The cache of each (sequence, K/V head) is cut into chunks of `split` keys.
+// A unit of work is one chunk of one K/V head for up to 16 of its query
+// heads; its K/V bytes are read from HBM once.  A small plan kernel counts
+// the units of every sequence (prefix sums in the workspace); the main kernel
+// is persistent: every wave walks its own list of units (unit ids w, w + W,
+// ... for W waves in the grid) and streams their 32-key tiles continuously:
+//  * tiles go HBM -> LDS through a private 2-stage ring per wave, filled by
+//    global_load_lds_dwordx4 (no staging registers, no workgroup barrier:
+//    a wave waits only for its own copies); the ring keeps streaming across
+//    unit boundaries, so there is no per-unit pipeline drain or refill;
 //  * K rows are stored 272 bytes apart (17 16-byte slots: 16 consecutive rows
 //    of one column hit 16 distinct bank slots) and V rows 288 bytes apart
 //    (18 = 2 mod 16: the 8 rows x 32 bytes a half-wave reads through the
-//    transposing load hit 16 distinct slots), so all LDS reads are
-//    conflict-free and every address is base + immediate;
-//  * per tile: S^T = K q^T with v_mfma_f32_16x16x32_bf16 (the group's heads are
-//    the 16 columns), online softmax per head column, then O^T = V^T P^T with
-//    V^T read by ds_read_b64_tr_b16 and the rounded probabilities as the B
-//    operand;
-//  * the four waves' (m, l, O) are merged through LDS, and the chunk's
-//    normalised partial output and log-sum-exp go to the workspace; a second
-//    kernel merges the chunks of each (sequence, head): L = log sum_s exp(L_s),
-//    O = sum_s exp(L_s - L) O_s, the FlashAttention-2 state merge
-//    ("Attention Engineering ...", section 4).
+//    transposing load hit 16 distinct slots); all addresses are base + imm;
+//  * per tile: S^T = K q^T with v_mfma_f32_16x16x32_bf16 (the group's heads
+//    are the 16 columns), online softmax per head column, then O^T = V^T P^T
+//    with V^T read by ds_read_b64_tr_b16 and the rounded probabilities as the
+//    B operand;
+//  * at the end of a unit the wave writes the chunk's normalised partial
+//    output and log-sum-exp; a second kernel merges the chunks of each
+//    (sequence, head): L = log sum_s exp(L_s), O = sum_s exp(L_s - L) O_s,
+//    the FlashAttention-2 state merge ("Attention Engineering ...", section 4).
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -41,7 +42,7 @@ namespace {
 
 constexpr int D = 128;
 constexpr int BN = 32;                    // keys per tile
-constexpr int NW = 4;                     // waves per workgroup
+constexpr int NW = 4;                     // waves per workgroup (independent)
 constexpr int KROW = D * 2 + 16;          // 272 B
 constexpr int VROW = D * 2 + 32;          // 288 B
 constexpr int KREG = BN * KROW;           // 8704 B
@@ -54,10 +55,47 @@ constexpr float TAU = 8.0f;
 struct Params {
     const __bf16 *q, *k, *v;
     const int32_t *seq_lens;
+    const int32_t *plan;                  // [B+1] unit prefix sums
     float *ws_o, *ws_lse;
-    int S_max, hq, hkv, G, n_hchunk;
+    int B, S_max, hq, hkv, G, n_hchunk;
     int split, n_split_max, window;
     float scale_log2;
+};
+
+// pre[b] = number of units of sequences 0..b-1; units of a sequence are
+// ceil(len / split) chunks x h_kv x n_hchunk.
+__global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *seq_lens, int B, int S_max,
+                                                           int split, int mult, int32_t *pre) {
+    __shared__ int sc[1024];
+    int carry = 0;
+    const int t = threadIdx.x;
+    if (t == 0) pre[0] = 0;
+    for (int base = 0; base < B; base += 1024) {
+        const int b = base + t;
+        int cnt = 0;
+        if (b < B) {
+            int len = seq_lens[b];
+            len = len < 0 ? 0 : (len > S_max ? S_max : len);
+            cnt = (len + split - 1) / split * mult;
+        }
+        sc[t] = cnt;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {         // inclusive scan
+            const int v = t >= off ? sc[t - off] : 0;
+            __syncthreads();
+            sc[t] += v;
+            __syncthreads();
+        }
+        if (b < B) pre[b + 1] = carry + sc[t];
+        carry += sc[1023];
+        __syncthreads();
+    }
+}
+
+struct Unit {
+    int b, g, hc, c;      // sequence, K/V head, head chunk, chunk index
+    int lo, hi;           // visible key range of the chunk
+    int n_tiles;
 };
 
 __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) {
@@ -67,188 +105,183 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int j16 = lane & 15;
     const int q16 = lane >> 4;
-
-    const int s = blockIdx.x;
-    const int g = blockIdx.y / p.n_hchunk;
-    const int hc = blockIdx.y % p.n_hchunk;
-    const int b = blockIdx.z;
-    int len = p.seq_lens[b];
-    len = len < 0 ? 0 : (len > p.S_max ? p.S_max : len);
-    if (s * p.split >= len) return;                      // beyond the sequence: unused split
-    const int kvis = p.window > 0 ? max(0, len - p.window) : 0;
-    const int lo = max(s * p.split, kvis);
-    const int hi = min((s + 1) * p.split, len);
-    const int n_tiles = lo < hi ? (hi - lo + BN - 1) / BN : 0;
-    // this wave's tiles: w, w + NW, ...
-    const int my_tiles = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
-
-    const int hidx = hc * 16 + j16;                       // head within the group (column)
-    const bool head_ok = hidx < p.G;
-    const int h = g * p.G + hidx;
-    const size_t kv_base = ((size_t)b * p.hkv + g) * (size_t)p.S_max * D;
-    const char *kg = reinterpret_cast<const char *>(p.k + kv_base);
-    const char *vg = reinterpret_cast<const char *>(p.v + kv_base);
+    const int wid = blockIdx.x * NW + wave;
+    const int nwaves = gridDim.x * NW;
+    const int total = ld_uniform(p.plan, p.B);
     char *ring = smem + wave * WAVE_BYTES;
 
-    // Per-lane DMA sources, relative to the tile's first key: block i of a
-    // stage covers stage bytes [1024 i, 1024 i + 1024); lane byte o = 1024 i +
-    // 16 lane holds K row o / 272 (o < 8704) or V row (o - 8704) / 288, chunk
-    // (remainder) / 16 (pad slots and bytes past the last row take a valid
-    // chunk of the last row).  rel_row[i] is that row, src[i] the row-0 address.
-    int rel_row[STAGE_BLK];
-    const char *src[STAGE_BLK];
+    // Unit id -> geometry.  Each cursor visits increasing unit ids, so its
+    // sequence index is found by walking forward from its previous one.
+    auto describe = [&](int u, int &walk_b) {
+        while (walk_b + 1 < p.B && ld_uniform(p.plan, walk_b + 1) <= u) ++walk_b;
+        Unit d;
+        d.b = walk_b;
+        int len = ld_uniform(p.seq_lens, d.b);
+        len = len < 0 ? 0 : (len > p.S_max ? p.S_max : len);
+        const int nc = (len + p.split - 1) / p.split;
+        const int r = u - ld_uniform(p.plan, d.b);
+        const int gh = r / nc;
+        d.c = r - gh * nc;
+        d.g = gh / p.n_hchunk;
+        d.hc = gh - d.g * p.n_hchunk;
+        const int kvis = p.window > 0 ? max(0, len - p.window) : 0;
+        d.lo = max(d.c * p.split, kvis);
+        d.hi = min((d.c + 1) * p.split, len);
+        d.n_tiles = d.lo < d.hi ? (d.hi - d.lo + BN - 1) / BN : 0;
+        return d;
+    };
+
+    // Per-lane DMA offsets inside a tile: block i of a stage covers stage
+    // bytes [1024 i, 1024 i + 1024); lane byte o = 1024 i + 16 lane holds K row
+    // o / 272 (o < 8704) or V row (o - 8704) / 288, chunk (remainder) / 16
+    // (pad slots and bytes past the last row take a valid chunk of the last
+    // row).
+    int rel_row[STAGE_BLK], col_off[STAGE_BLK];
+    unsigned is_v_mask = 0;
 #pragma unroll
     for (int i = 0; i < STAGE_BLK; ++i) {
         const int o = i * 1024 + lane * 16;
         const bool is_v = o >= KREG;
         const int ro = is_v ? o - KREG : o;
         const int r = min(is_v ? ro / VROW : ro / KROW, BN - 1);
-        const int ch = min((ro - r * (is_v ? VROW : KROW)) >> 4, D / 8 - 1);
         rel_row[i] = r;
-        src[i] = (is_v ? vg : kg) + ch * 16;
+        col_off[i] = min((ro - r * (is_v ? VROW : KROW)) >> 4, D / 8 - 1) * 16;
+        is_v_mask |= (unsigned)is_v << i;
     }
-    auto issue = [&](int j) {                             // j-th tile of this wave
-        const int t0 = lo + (wave + NW * j) * BN;
-        char *stage = ring + (j & 1) * STAGE_BYTES;
-        if (t0 + BN <= hi) {
-#pragma unroll
-            for (int i = 0; i < STAGE_BLK; ++i)
-                dma16(src[i] + (size_t)(t0 + rel_row[i]) * (D * 2), stage + i * 1024);
-        } else {
-#pragma unroll
-            for (int i = 0; i < STAGE_BLK; ++i)
-                dma16(src[i] + (size_t)min(t0 + rel_row[i], hi - 1) * (D * 2), stage + i * 1024);
+
+    // Fetch cursor: unit id fu (geometry fd), tile ft; fetched-tile counter nf.
+    int fu = wid, ft = 0, nf = 0, f_walk = 0;
+    Unit fd;
+    if (fu < total) fd = describe(fu, f_walk);
+    auto fetch_skip_empty = [&]() {
+        while (fu < total && ft >= fd.n_tiles) {
+            fu += nwaves;
+            ft = 0;
+            if (fu < total) fd = describe(fu, f_walk);
         }
     };
-    if (my_tiles > 0) issue(0);
-    if (my_tiles > 1) issue(1);
-
-    // q^T as B operand: column = head j16, d = 32ks + 8 q16 .. +7.
-    bf16x8 qop[4];
+    auto issue_next = [&]() {                        // issue the fetch cursor's tile
+        fetch_skip_empty();
+        if (fu >= total) return false;
+        const size_t kv_base = ((size_t)fd.b * p.hkv + fd.g) * (size_t)p.S_max * D;
+        const char *kg = reinterpret_cast<const char *>(p.k + kv_base);
+        const char *vg = reinterpret_cast<const char *>(p.v + kv_base);
+        const int t0 = fd.lo + ft * BN;
+        char *stage = ring + (nf & 1) * STAGE_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (head_ok) val = ldg16(p.q + ((size_t)b * p.hq + h) * D + 32 * ks + 8 * q16);
-        qop[ks] = __builtin_bit_cast(bf16x8, val);
-    }
+        for (int i = 0; i < STAGE_BLK; ++i) {
+            const int key = min(t0 + rel_row[i], fd.hi - 1);
+            const char *base = ((is_v_mask >> i) & 1) ? vg : kg;
+            dma16(base + (size_t)key * (D * 2) + col_off[i], stage + i * 1024);
+        }
+        ++ft;
+        ++nf;
+        return true;
+    };
 
-    f32x4 oacc[8];                                        // d = 16 db + 4 q16 + i, head j16
-#pragma unroll
-    for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
     // V^T operand: lane j of group q16 addresses V row 4 q16 + j/4 (second
     // read: +16), d = 16 db + 4 (j%4) .. +3: chunk 2 db + (j%4)/2, byte 8 (j%2).
     const int v_lane_off = KREG + (4 * q16 + (j16 >> 2)) * VROW + ((j16 & 3) >> 1) * 16 + 8 * (j16 & 1);
     const int k_lane_off = j16 * KROW + q16 * 16;
 
-    for (int j = 0; j < my_tiles; ++j) {
-        // stage j&1 landed; tile j+1 (if any) may still be in flight
-        if (j + 1 < my_tiles) wait_vmcnt<STAGE_BLK>(); else wait_vmcnt<0>();
-        const char *st = ring + (j & 1) * STAGE_BYTES;
-        const int t0 = lo + (wave + NW * j) * BN;
-        f32x4 sacc[2];
+    // Prime the ring.
+    bool more = issue_next();
+    if (more) issue_next();
+    int nc_done = 0;                                  // tiles consumed so far
+
+    int c_walk = 0;
+    for (int cu = wid; cu < total; cu += nwaves) {
+        const Unit d = describe(cu, c_walk);
+        const int hidx = d.hc * 16 + j16;
+        const bool head_ok = hidx < p.G;
+        const int h = d.g * p.G + hidx;
+        bf16x8 qop[4];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4 val = {0u, 0u, 0u, 0u};
+            if (head_ok) val = ldg16(p.q + ((size_t)d.b * p.hq + h) * D + 32 * ks + 8 * q16);
+            qop[ks] = __builtin_bit_cast(bf16x8, val);
+        }
+        f32x4 oacc[8];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(st + k_lane_off + 16 * mb * KROW + 64 * ks);
-                sacc[mb] = mfma16x16x32(a, qop[ks], sacc[mb]);
+        for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY, l_run = 0.f;
+
+        for (int j = 0; j < d.n_tiles; ++j) {
+            // this tile is the nc_done-th fetched; a later one may be in flight
+            if (nf > nc_done + 1) wait_vmcnt<STAGE_BLK>(); else wait_vmcnt<0>();
+            const char *st = ring + (nc_done & 1) * STAGE_BYTES;
+            const int t0 = d.lo + j * BN;
+            f32x4 sacc[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(st + k_lane_off + 16 * mb * KROW + 64 * ks);
+                    sacc[mb] = mfma16x16x32(a, qop[ks], sacc[mb]);
+                }
             }
-        }
-        // element (mb, i) of this lane is key t0 + 16 mb + 4 q16 + i of head column j16
-        const bool tail = t0 + BN > hi;
-        float x[8];
-        float mx = -INFINITY;
+            // element (mb, i) of this lane is key t0 + 16 mb + 4 q16 + i of head column j16
+            const bool tail = t0 + BN > d.hi;
+            float x[8];
+            float mx = -INFINITY;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v = sacc[mb][i] * p.scale_log2;
-                if (tail) v = (t0 + 16 * mb + 4 * q16 + i < hi) ? v : -INFINITY;
-                x[4 * mb + i] = v;
-                mx = fmaxf(mx, v);
+                for (int i = 0; i < 4; ++i) {
+                    float v = sacc[mb][i] * p.scale_log2;
+                    if (tail) v = (t0 + 16 * mb + 4 * q16 + i < d.hi) ? v : -INFINITY;
+                    x[4 * mb + i] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const bool upd = mx > m_run + TAU;
+            const float m_new = upd ? mx : m_run;
+            const float alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
+            m_run = m_new;
+            if (__any(upd)) {
+#pragma unroll
+                for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
             }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const bool upd = mx > m_run + TAU;
-        const float m_new = upd ? mx : m_run;
-        const float alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
-        m_run = m_new;
-        if (__any(upd)) {
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            float pv[8];
+            float lsum = 0.f;
 #pragma unroll
-            for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
-        }
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        float pv[8];
-        float lsum = 0.f;
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = fast_exp2(x[e] - m_use);
+                lsum += pv[e];
+            }
+            l_run = l_run * alpha + lsum;
+            const bf16x8 pop = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pv[e] = fast_exp2(x[e] - m_use);
-            lsum += pv[e];
-        }
-        l_run = l_run * alpha + lsum;
-        const bf16x8 pop = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-            const bf16x4 lo4 = lds_read_tr16(st + v_lane_off + 32 * db);
-            const bf16x4 hi4 = lds_read_tr16(st + v_lane_off + 16 * VROW + 32 * db);
-            const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[db] = mfma16x16x32(a, pop, oacc[db]);
-        }
-        // refill the stage with tile j+2 once every read of it has returned
-        if (j + 2 < my_tiles) {
+            for (int db = 0; db < 8; ++db) {
+                const bf16x4 lo4 = lds_read_tr16(st + v_lane_off + 32 * db);
+                const bf16x4 hi4 = lds_read_tr16(st + v_lane_off + 16 * VROW + 32 * db);
+                const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[db] = mfma16x16x32(a, pop, oacc[db]);
+            }
+            ++nc_done;
+            // refill the consumed stage once every read of it has returned
             asm volatile("" ::: "memory");
             wait_lgkmcnt0();
-            issue(j + 2);
+            if (more) more = issue_next();
         }
-    }
-    float lt = l_run + shfl_xor(l_run, 16);
-    lt += shfl_xor(lt, 32);
-
-    // Merge the four waves through LDS (reusing the rings).
-    wait_vmcnt<0>();
-    __syncthreads();
-    float *red = reinterpret_cast<float *>(smem);        // [NW][16 heads][D] + m, l
-    float *red_m = red + NW * 16 * D;
-    float *red_l = red_m + NW * 16;
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-        *reinterpret_cast<f32x4 *>(red + (wave * 16 + j16) * D + 16 * db + 4 * q16) = oacc[db];
-    if (q16 == 0) {
-        red_m[wave * 16 + j16] = m_run;
-        red_l[wave * 16 + j16] = lt;
-    }
-    __syncthreads();
-    {
-        const int hh = tid >> 4;                          // 16 heads x 16 threads
-        const int d0 = (tid & 15) * 8;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w * 16 + hh]);
-        const float Mu = (M == -INFINITY) ? 0.f : M;
-        float L = 0.f, wgt[NW];
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            wgt[w] = fast_exp2(red_m[w * 16 + hh] - Mu);
-            L += wgt[w] * red_l[w * 16 + hh];
-        }
-        const float inv = L > 0.f ? 1.0f / L : 0.f;
-        const int hidx2 = hc * 16 + hh;
-        if (hidx2 < p.G) {
-            const int h2 = g * p.G + hidx2;
-            const size_t ws = (((size_t)b * p.hq + h2) * p.n_split_max + s);
+        // the unit's partial result (an empty unit writes O = 0, L = -inf)
+        float lt = l_run + shfl_xor(l_run, 16);
+        lt += shfl_xor(lt, 32);
+        if (head_ok) {
+            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+            const size_t ws = (((size_t)d.b * p.hq + h) * p.n_split_max + d.c);
             float *wo = p.ws_o + ws * D;
 #pragma unroll
-            for (int dd = 0; dd < 8; ++dd) {
-                float acc = 0.f;
-#pragma unroll
-                for (int w = 0; w < NW; ++w) acc += wgt[w] * red[(w * 16 + hh) * D + d0 + dd];
-                wo[d0 + dd] = acc * inv;
-            }
-            if ((tid & 15) == 0) p.ws_lse[ws] = L > 0.f ? Mu + __log2f(L) : -INFINITY;
+            for (int db = 0; db < 8; ++db)
+                *reinterpret_cast<f32x4 *>(wo + 16 * db + 4 * q16) = oacc[db] * inv;
+            if (q16 == 0) p.ws_lse[ws] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
         }
     }
+    wait_vmcnt<0>();
 }
 
 // One wave per (head, sequence): merge the partials of the sequence's splits.
@@ -294,8 +327,10 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
     p.k = static_cast<const __bf16 *>(a.k_cache);
     p.v = static_cast<const __bf16 *>(a.v_cache);
     p.seq_lens = a.seq_lens;
+    p.plan = a.plan;
     p.ws_o = a.ws_o;
     p.ws_lse = a.ws_lse;
+    p.B = a.B;
     p.S_max = a.S_max;
     p.hq = a.hq;
     p.hkv = a.hkv;
@@ -305,16 +340,26 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
     p.n_split_max = a.n_split_max;
     p.window = a.window;
     p.scale_log2 = a.scale * kLog2e;
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a.seq_lens, a.B, a.S_max,
+                       a.split, a.hkv * p.n_hchunk, a.plan);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)decode_bf16_d128_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        e = hipFuncSetAttribute((const void *)decode_bf16_d128_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    dim3 grid(a.n_split_max, a.hkv * p.n_hchunk, a.B);
-    hipLaunchKernelGGL(decode_bf16_d128_kernel, grid, dim3(64 * NW), LDS_BYTES, stream, p);
-    hipError_t e = hipGetLastError();
+    // persistent grid: one workgroup per CU (its LDS takes most of the CU),
+    // never more workgroups than the largest possible number of units needs
+    const long long max_units = (long long)a.B * a.hkv * p.n_hchunk * a.n_split_max;
+    long long blocks = (max_units + NW - 1) / NW;
+    if (blocks > a.num_cus) blocks = a.num_cus;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(decode_bf16_d128_kernel, dim3((unsigned)blocks), dim3(64 * NW), LDS_BYTES,
+                       stream, p);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_combine(a.ws_o, a.ws_lse, a.seq_lens, a.o, a.lse, a.B, a.hq, D, a.S_max,
                                 a.split, a.n_split_max, stream);

@@ -124,6 +124,14 @@ __device__ __forceinline__ void raw_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
+// Read-only load with a wave-uniform index through the constant address
+// space: the compiler emits a scalar load (tracked by lgkmcnt, so it does not
+// wait for outstanding vector-memory copies).  The data must not change
+// while the kernel runs.
+__device__ __forceinline__ int ld_uniform(const int32_t *p, int i) {
+    return ((const __attribute__((address_space(4))) int32_t *)p)[i];
+}
+
 // LDS byte offset of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char *)p);

@@ -33,6 +33,8 @@ struct DecodeArgs {
     int n_split_max;      // ceil(S_max / split)
     float *ws_o;          // [B, hq, n_split_max, d]
     float *ws_lse;        // [B, hq, n_split_max]  (log2 units)
+    int32_t *plan;        // [B + 1] unit prefix sums (workspace)
+    int num_cus;          // compute units of the device (persistent grid size)
 };
 hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream);
 
