@@ -17,7 +17,10 @@ two device synchronisations; kernel durations come from HIP events recorded
 on the stream the kernels run on.  One JSON line is printed.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|decode|mla|swa-mha|swa-mqa]
+                    [--only prefill|decode|mla|swa-mha|swa-mqa|copy]
+
+``--only copy`` times a plain 1 GiB device copy instead: it is the
+calibration run for rocprofv3's HBM byte counters, not an attention bench.
 """
 from __future__ import annotations
 
@@ -32,7 +35,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 # rocprofv3 FETCH_SIZE/WRITE_SIZE summaries (KiB per dispatch), scaled by the
 # same counters read on a plain copy kernel of known size; None until taken
 # for the current kernel.
-PREFILL_TRAFFIC_BYTES = None
+PREFILL_TRAFFIC_BYTES = 212404173   # prefill_bf16_d128 kernel <1,2,4>, FETCH x2.000 + WRITE x1.000
 
 
 def prefill_visible_pairs(T: int, causal: bool, window: int) -> int:
@@ -97,6 +100,20 @@ def bench_decode(torch, ta, W, steps, warmup):
     del q, kc, vc, o, ws
     return {"ms": ms, "wall_s": wall, "bytes": cache_bytes + io_bytes, "sum_len": total_len,
             "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+
+
+def bench_copy(torch, steps, warmup, nbytes=1 << 30):
+    """A plain device-to-device copy of known size (reads and writes nbytes
+    each).  Not part of the attention path: its HBM counter readings give the
+    scale factor between rocprofv3's FETCH_SIZE/WRITE_SIZE and bytes."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    ms, wall = _events_time(torch, lambda: dst.copy_(src), steps, warmup, stream)
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    del src, dst
+    return {"ms": ms, "wall_s": wall, "bytes": 2 * nbytes, "gbs": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
 def bench_mla(torch, ta, W, steps, warmup, copies=3):
@@ -164,7 +181,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    choices=["prefill", "decode", "mla", "swa-mha", "swa-mqa"])
+                    choices=["prefill", "decode", "mla", "swa-mha", "swa-mqa", "copy"])
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -192,6 +209,8 @@ def main(argv=None):
         out["swa_mha"] = bench_prefill(torch, ta, W, W.SWA_MHA, args.steps, args.warmup)
     if only == "swa-mqa":
         out["swa_mqa"] = bench_prefill(torch, ta, W, W.SWA_MQA, args.steps, args.warmup)
+    if only == "copy":
+        out["copy"] = bench_copy(torch, args.steps, args.warmup)
     if only in (None, "decode"):
         out["decode"] = bench_decode(torch, ta, W, args.steps, args.warmup)
         print(f"[bench] decode {out['decode']['ms']:.3f} ms {out['decode']['gbs']:.0f} GB/s",

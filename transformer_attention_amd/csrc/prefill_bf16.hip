@@ -27,11 +27,11 @@
 //    transposing LDS load ds_read_b64_tr_b16 (two per operand), whose four
 //    source rows are exactly the four keys each lane's P values belong to;
 //  * K and V tiles (64 keys) are stored row-major in LDS with padded rows so
-//    every LDS address stays base + immediate and reads are bank-conflict
-//    free: K rows are 304 bytes apart (19 16-byte slots, 19 = 3 mod 16, so 16
-//    consecutive rows of one column hit 16 distinct slots), V rows 320 bytes
-//    apart (20 = 4 mod 16, so the 4 rows x 64 bytes a 32-lane half-wave
-//    reads through the transposing load hit 16 distinct slots);
+//    every LDS address stays base + immediate: rows are 304 bytes apart (19
+//    16-byte slots, 19 = 3 mod 16), so the 16 consecutive rows of one column
+//    that the K reads touch hit 16 distinct slots; the transposing V reads
+//    share the stride (a 320-byte V stride, conflict-free for them, measured
+//    slower overall because it costs LDS capacity and ring depth);
 //  * K/V tiles stream HBM -> LDS through a 4-stage ring filled by
 //    global_load_lds_dwordx4 (no staging registers): while a wave computes
 //    the scores of tile t+1 and the P.V product of tile t, tiles t+2 and t+3
