@@ -150,6 +150,14 @@ __device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base) {
                  :: "v"(gsrc), "s"(m0v) : "memory");
 }
 
+// Same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the saddr form: one VGPR per address instead of two).
+__device__ __forceinline__ void dma16_off(const void *gbase, uint32_t off, const void *lds_base) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_offset(lds_base));
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(gbase), "s"(m0v) : "memory");
+}
+
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 // ds_read_b64_tr_b16: within each 16-lane group, result lane i element r is
 // the (i%4)-th bf16 of the 8 bytes addressed by lane 4r + i/4 of that group.

@@ -16,17 +16,22 @@
 //  * 32-token tiles [32 x 576 bf16 = 36 KB] stream HBM -> LDS through a
 //    4-stage ring filled by global_load_lds_dwordx4 (no staging registers),
 //    three tiles in flight per CU while the fourth is consumed;
-//  * each tile is stored once, row-major with its 16-byte chunks XOR-swizzled
-//    per row; the score product reads it with 16-byte loads, the P.V product
-//    reads the first 512 columns transposed with ds_read_b64_tr_b16, so the
-//    latent is never copied;
-//  * 8 waves (two per SIMD), each owning 16 heads: S^T = K Q^T with
-//    v_mfma_f32_16x16x32_bf16 (the wave's 16 queries, 576 wide, stay in
-//    registers as B operands), then O^T[512 x 16] += C^T P^T with the rounded
-//    probabilities as the B operand (the two 16-token halves of the tile
-//    form the 32-token K dimension);
-//  * the online-softmax state is per head (one lane column), and the
-//    reference max only moves when a tile exceeds it by 2^8.
+//  * each tile is stored once, row-major with rows padded to 1168 bytes; the
+//    score product reads it with 16-byte loads, the P.V product reads the
+//    first 512 columns transposed with ds_read_b64_tr_b16, so the latent is
+//    never copied;
+//  * 4 waves (one per SIMD, up to 512 registers each), each owning 32 heads:
+//    S^T[32 tokens x 32 heads] = K Q^T with v_mfma_f32_32x32x16_bf16 (the
+//    wave's 32 queries, 576 wide, stay in registers as B operands), then
+//    O^T[512 x 32 heads] += C^T P^T with the rounded probabilities as the B
+//    operand straight from the score accumulator.  Every 16-byte LDS read
+//    feeds a 32x32x16 MFMA, half the LDS bytes per FLOP of a 16-head split;
+//  * the online-softmax state is per head (one lane column; the two lane
+//    halves hold the two 16-token halves of a tile and share the max), and
+//    the reference max only moves when a tile exceeds it by 2^8;
+//  * the workgroup id runs over sequences fastest, so with a batch that is a
+//    multiple of 8 all chunks of one sequence run on one XCD and share its
+//    L2 for the query rows.
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -36,43 +41,109 @@ namespace {
 constexpr int DC = 512, DR = 64, DK = DC + DR;
 constexpr int TB = 32;                    // tokens per tile
 constexpr int ROWB = DK * 2;              // 1152 bytes per cache row in HBM
-constexpr int LROW = ROWB + 16;           // LDS row stride: 73 16-byte slots
-constexpr int TILE_BYTES = 37 * 1024;     // 32 padded rows (37376 B) rounded up to whole DMA blocks
+constexpr int LROW_SLOTS = 76;            // LDS row pitch in 16-byte slots (72 data + 4 pad)
+constexpr int LROW = LROW_SLOTS * 16;     // 1216 bytes
+constexpr int TILE_BYTES = 38 * 1024;     // 32 rows (last row ends at slot 2432) = 38 DMA blocks
 constexpr int NSTAGE = 4;
 constexpr int LDS_BYTES = NSTAGE * TILE_BYTES;   // 151552
-constexpr int NW = 8;                     // waves per workgroup
-constexpr int HPW = 16;                   // heads per wave
+constexpr int NW = 4;                     // waves per workgroup
+constexpr int HPW = 32;                   // heads per wave
 constexpr int HPC = NW * HPW;             // heads per workgroup (chunk)
-constexpr int NBLK = TILE_BYTES / 1024;   // 37 one-KB DMA blocks per tile:
-                                          // waves 0-4 issue 5, waves 5-7 issue 4
+constexpr int NBLK = TILE_BYTES / 1024;   // 38 one-KB DMA blocks per tile:
+                                          // waves 0-1 issue 10, waves 2-3 issue 9
 constexpr float TAU = 8.0f;
 
 struct Params {
     const __bf16 *q, *c;
     const int32_t *seq_lens;
     float *ws_o, *ws_lse;
-    int S_max, H;
-    int split, n_split_max;
+    int B, S_max, H;
+    int split, n_split_max, n_hchunk;
     float scale_log2;
 };
 
-// Row r of a tile starts at 1168 r: 1168 = 73 * 16 and 73 = 9 (mod 16), so
-// 16 consecutive rows fall in 16 distinct 16-byte bank slots (conflict-free
-// 16-byte reads down a column) and 4 consecutive rows x 32 bytes fall in 8
-// distinct slots (conflict-free transposing reads); addresses stay affine.
-__device__ __forceinline__ int tile_off(int r, int chunk) { return r * LROW + (chunk << 4); }
+// Row r of a tile starts at slot 76 r + rho(r), rho(r) = (r / 4) mod 4, and
+// holds its 72 16-byte chunks contiguously (4 pad slots per row).  With 64
+// four-byte banks (16 slots):
+//  * 16 consecutive rows at one chunk (the 16-byte score-operand reads of a
+//    quarter wave) hit slots 12 r + rho(r) + c = 16 distinct values;
+//  * 4 rows 4j..4j+3 x 64 bytes (what a half wave reads through the
+//    transposing load) start at slots 12 i + rho + const, i.e. four disjoint
+//    4-slot groups;
+// so neither read pattern has bank conflicts, and every address stays affine
+// in the loop indices.
+__device__ __forceinline__ int row_slot(int r) { return LROW_SLOTS * r + ((r >> 2) & 3); }
 
-__global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(Params p) {
+// The score product as inline asm with a VGPR accumulator.  Hazards the
+// compiler cannot see through asm are covered here: the first MFMA of a chain
+// waits 5 cycles (VALU writes of its operands just before), consecutive
+// MFMAs of one chain accumulate into the same registers with the same opcode
+// (forwarded by the hardware), and the last one is followed by 19 wait states
+// before any VALU instruction may read the 16-pass result.  Operands coming
+// from LDS or global loads are covered by the waitcnts the compiler inserts
+// for every asm register operand.
+__device__ __forceinline__ f32x16 mfma_s_first(bf16x8 a, bf16x8 b) {
+    f32x16 d;
+    asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+__device__ __forceinline__ f32x16 mfma_s_acc(bf16x8 a, bf16x8 b, f32x16 c) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+    return c;
+}
+__device__ __forceinline__ f32x16 mfma_s_last(bf16x8 a, bf16x8 b, f32x16 c) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
+                 : "+v"(c) : "v"(a), "v"(b));
+    return c;
+}
+
+// acc *= f on an accumulator held in AGPRs, as asm so that the (rare)
+// conditional rescale does not make the compiler move the 256 output
+// registers through VGPRs around the branch.  The trailing wait states cover
+// the AGPR writes before the next MFMA reads them as its accumulator.
+__device__ __forceinline__ void scale_acc(f32x16 &acc, float f) {
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %[t], %[a0]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a0], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a1]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a1], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a2]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a2], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a3]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a3], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a4]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a4], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a5]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a5], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a6]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a6], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a7]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a7], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a8]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a8], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a9]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a9], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a10]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a10], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a11]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a11], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a12]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a12], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a13]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a13], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a14]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a14], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a15]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a15], %[t]\n\t"
+        "s_nop 4"
+        : [a0] "+a"(acc[0]), [a1] "+a"(acc[1]), [a2] "+a"(acc[2]), [a3] "+a"(acc[3]),
+          [a4] "+a"(acc[4]), [a5] "+a"(acc[5]), [a6] "+a"(acc[6]), [a7] "+a"(acc[7]),
+          [a8] "+a"(acc[8]), [a9] "+a"(acc[9]), [a10] "+a"(acc[10]), [a11] "+a"(acc[11]),
+          [a12] "+a"(acc[12]), [a13] "+a"(acc[13]), [a14] "+a"(acc[14]), [a15] "+a"(acc[15]),
+          [t] "=&v"(t)
+        : [f] "v"(f));
+}
+
+__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_kernel(Params p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int q16 = lane >> 4;
-    const int j16 = lane & 15;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;                 // lane half: which 16 tokens of a tile
 
-    const int s = blockIdx.x;
-    const int hc = blockIdx.y;
-    const int b = blockIdx.z;
+    // workgroup id -> (sequence fastest, split, head chunk)
+    const int id = blockIdx.x;
+    const int b = id % p.B;
+    const int rest = id / p.B;
+    const int s = rest % p.n_split_max;
+    const int hc = rest / p.n_split_max;
     int len = p.seq_lens[b];
     len = len < 0 ? 0 : (len > p.S_max ? p.S_max : len);
     if (s * p.split >= len) return;
@@ -87,20 +158,39 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(Params p) {
     // (row o / 1168, chunk (o % 1168) / 16); the pad slot (chunk 72) and the
     // bytes past row 31 receive an arbitrary valid chunk.  Rows past the
     // chunk end re-read the last valid row (their scores are masked).
-    const int my_blk0 = wave < 5 ? 5 * wave : 25 + 4 * (wave - 5);
-    const int my_nblk = wave < 5 ? 5 : 4;
+    const int my_blk0 = wave < 2 ? 10 * wave : 20 + 9 * (wave - 2);
+    const int my_nblk = wave < 2 ? 10 : 9;
+    // Byte offset (within a tile's 32 cache rows) that lane `lane` copies for
+    // each of this wave's blocks; pad slots re-read a valid chunk.
+    uint32_t dma_off[10];
+    int dma_row[10];
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const int q = (my_blk0 + min(i, my_nblk - 1)) * 64 + lane;     // slot index in the tile
+        const int r = q / LROW_SLOTS;
+        const int c = min(max(q - row_slot(r), 0), DK / 8 - 1);
+        dma_row[i] = r;
+        dma_off[i] = (uint32_t)(r * ROWB + c * 16);
+    }
     auto issue_tile = [&](int t) {
         char *stage = smem + (t % NSTAGE) * TILE_BYTES;
         const int t0 = lo + t * TB;
+        const char *gbase = cg + (size_t)t0 * ROWB;
+        const int last = hi_tok - 1 - t0;       // last valid row of this tile
+        if (last >= TB - 1) {
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            if (i >= my_nblk) break;
-            const int blk = my_blk0 + i;
-            const int o = blk * 1024 + lane * 16;
-            const int r = min(o / LROW, TB - 1);
-            const int ch = min((o - (o / LROW) * LROW) >> 4, DK / 8 - 1);
-            const int tok = min(t0 + r, hi_tok - 1);
-            dma16(cg + (size_t)tok * ROWB + ch * 16, stage + blk * 1024);
+            for (int i = 0; i < 10; ++i) {
+                if (i >= my_nblk) break;
+                dma16_off(gbase, dma_off[i], stage + (my_blk0 + i) * 1024);
+            }
+        } else {                                // ragged last tile: rows past the end re-read the last row
+#pragma unroll
+            for (int i = 0; i < 10; ++i) {
+                if (i >= my_nblk) break;
+                const uint32_t off = dma_row[i] > last
+                    ? dma_off[i] - (uint32_t)((dma_row[i] - last) * ROWB) : dma_off[i];
+                dma16_off(gbase, off, stage + (my_blk0 + i) * 1024);
+            }
         }
     };
 
@@ -109,114 +199,158 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_decode_kernel(Params p) {
     for (int t = 0; t < NSTAGE - 1; ++t)
         if (t < n_tiles) issue_tile(t);
 
-    // The wave's 16 queries as B operands: head = hc*128 + 16*wave + j16,
-    // d = 32ks + 8*q16 .. +7.
-    const int h = hc * HPC + wave * HPW + j16;
+    // The wave's 32 queries as B operands: head = hc*128 + 32*wave + l32,
+    // d = 16ks + 8*hh .. +7.
+    const int h = hc * HPC + wave * HPW + l32;
     const bool head_ok = h < p.H;
-    bf16x8 qop[DK / 32];
+    bf16x8 qop[DK / 16];
+    {
+        const __bf16 *qrow = p.q + ((size_t)b * p.H + (head_ok ? h : 0)) * DK + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (head_ok) val = ldg16(p.q + ((size_t)b * p.H + h) * DK + 32 * ks + 8 * q16);
-        qop[ks] = __builtin_bit_cast(bf16x8, val);
+        for (int ks = 0; ks < DK / 16; ++ks) {
+            u32x4 val = ldg16(qrow + 16 * ks);
+            if (!head_ok) val = u32x4{0u, 0u, 0u, 0u};
+            qop[ks] = __builtin_bit_cast(bf16x8, val);
+        }
     }
 
-    f32x4 oacc[DC / 16];
+    f32x16 oacc[DC / 32];
 #pragma unroll
-    for (int db = 0; db < DC / 16; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < DC / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    // C^T operand (16 d x 32 tokens) through the transposing read: lane j of
-    // 16-lane group q16 addresses token row 4*q16 + j/4 (second read: +16),
-    // d = 16db + 4(j%4) .. +3, i.e. chunk 2db + (j%4)/2, byte 8(j%2).
-    const int v_row_lane = 4 * q16 + (j16 >> 2);
-    const int v_chunk_lane = (j16 & 3) >> 1;
-    const int v_byte_lane = 8 * (j16 & 1);
+    // C^T operand (32 d x 16 tokens) through the transposing read.  K slot j
+    // of lane half hh in token step kk is token 16kk + 8(j/4) + 4hh + (j%4),
+    // the order in which the score accumulator holds the probabilities.  Lane
+    // L of 16-lane group G addresses token row 16kk + 4(G/2) + L/4 (second
+    // read: +8) at d = 32db + 16(G%2) + 4(L%4), so result lane i of group G
+    // receives d = 32db + 16(G%2) + i, i.e. A row l % 32.
+    const int g16 = lane >> 4;
+    const int L16 = lane & 15;
+    // token row 16kk + 4(G/2) + L/4 (+8): rho = G/2 (+2), independent of kk
+    const int v_byte_lane = LROW * (4 * (g16 >> 1) + (L16 >> 2)) + 16 * (g16 >> 1) +
+                            32 * (g16 & 1) + 8 * (L16 & 3);
 
+    constexpr int NKS = DK / 16;              // 36 k-steps of the score product
+    constexpr int PF = 3;                     // LDS operand loads issued ahead of their MFMA
     for (int t = 0; t < n_tiles; ++t) {
         // Tile t landed once at most (NSTAGE-2) newer tiles are pending.  The
         // q loads above were issued after the prologue DMAs, so the first
         // iteration waits for everything.
         const int newer = t == 0 ? 0 : min(NSTAGE - 2, n_tiles - 1 - t);
         if (newer == 0) wait_vmcnt<0>();
-        else if (newer == 1) { if (my_nblk == 5) wait_vmcnt<5>(); else wait_vmcnt<4>(); }
-        else { if (my_nblk == 5) wait_vmcnt<10>(); else wait_vmcnt<8>(); }
+        else if (newer == 1) { if (my_nblk == 10) wait_vmcnt<10>(); else wait_vmcnt<9>(); }
+        else { if (my_nblk == 10) wait_vmcnt<20>(); else wait_vmcnt<18>(); }
         raw_barrier();                          // every wave's part of tile t is in LDS,
                                                 // and stage (t-1) is no longer read
-        if (t + NSTAGE - 1 < n_tiles) issue_tile(t + NSTAGE - 1);
 
         const char *kt = smem + (t % NSTAGE) * TILE_BYTES;
         const int t0 = lo + t * TB;
-        // S^T (two 16-token blocks x 16 heads): token 16mb + j16, d chunk 4ks + q16
-        f32x4 sacc[2];
+        // S^T (32 tokens x 32 heads): A = token row l32, d chunk 2ks + hh.
+        // The operand of k-step ks + PF is loaded before the MFMA of k-step
+        // ks; the next tile's copies are issued after the first few MFMAs.
+        const char *krow = kt + 16 * (row_slot(l32) + hh);
+        bf16x8 ka[PF + 1];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < PF; ++i) ka[i] = *reinterpret_cast<const bf16x8 *>(krow + 32 * i);
+        f32x16 sacc;
 #pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + tile_off(16 * mb + j16, 4 * ks + q16));
-                sacc[mb] = mfma16x16x32(a, qop[ks], sacc[mb]);
-                if ((ks & 5) == 5) __builtin_amdgcn_sched_barrier(0);   // bound the load look-ahead
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (ks + PF < NKS)
+                ka[(ks + PF) % (PF + 1)] = *reinterpret_cast<const bf16x8 *>(krow + 32 * (ks + PF));
+            const bf16x8 a = ka[ks % (PF + 1)];
+            if (ks == 0) sacc = mfma_s_first(a, qop[0]);
+            else if (ks == NKS - 1) sacc = mfma_s_last(a, qop[ks], sacc);
+            else sacc = mfma_s_acc(a, qop[ks], sacc);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks == 2 && t + NSTAGE - 1 < n_tiles) {
+                issue_tile(t + NSTAGE - 1);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // element (mb, i) of this lane is token t0 + 16mb + 4*q16 + i of head column j16
-        const bool tail = t0 + TB > hi_tok;
-        float x[8];
+        // element i of this lane is token t0 + 8(i/4) + 4hh + (i%4) of head column l32
         float mx = -INFINITY;
+        if (t0 + TB > hi_tok) {                 // ragged last tile: mask the rows past the end
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v = sacc[mb][i] * p.scale_log2;
-                if (tail) {
-                    const int tok = t0 + 16 * mb + 4 * q16 + i;
-                    v = tok < hi_tok ? v : -INFINITY;
-                }
-                x[4 * mb + i] = v;
-                mx = fmaxf(mx, v);
+            for (int i = 0; i < 16; ++i) {
+                const int tok = t0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+                sacc[i] = tok < hi_tok ? sacc[i] : -INFINITY;
             }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+        mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
         const bool upd = mx > m_run + TAU;
         const float m_new = upd ? mx : m_run;
         const float alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
         m_run = m_new;
-        if (__any(upd)) {
+        if (t > 0 && __any(upd)) {              // before tile 0 the output is still zero
 #pragma unroll
-            for (int db = 0; db < DC / 16; ++db) oacc[db] *= alpha;
+            for (int db = 0; db < DC / 32; ++db) scale_acc(oacc[db], alpha);
         }
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        float pv[8];
+        // p = 2^(s * scale_log2 - m): one FMA and one exp per score
+        // (computed in place: sacc[i] becomes the probability of score i)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sacc[i] = fast_exp2(__builtin_fmaf(sacc[i], p.scale_log2, -m_use));
+        const bf16x8 pop0 = to_bf16x8(sacc[0], sacc[1], sacc[2], sacc[3], sacc[4], sacc[5], sacc[6], sacc[7]);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // O^T += C^T P^T: token step kk = 0 for all d-blocks (the second half
+        // of the probabilities is computed in the shadow of these MFMAs),
+        // then kk = 1.
+        const char *vbase = kt + v_byte_lane;
+        bf16x4 va[PF + 1][2];
+        auto vload = [&](int j, bf16x4 *dst) {     // j = kk * 16 + db
+            const char *vb = vbase + (16 * (j >> 4)) * LROW + 64 * (j & 15);
+            dst[0] = lds_read_tr16(vb);
+            dst[1] = lds_read_tr16(vb + 8 * LROW + 32);
+        };
+#pragma unroll
+        for (int i = 0; i < PF; ++i) vload(i, va[i]);
+        bf16x8 pop1;
         float lsum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pv[e] = fast_exp2(x[e] - m_use);
-            lsum += pv[e];
+        for (int j = 0; j < 2 * (DC / 32); ++j) {
+            if (j + PF < 2 * (DC / 32)) vload(j + PF, va[(j + PF) % (PF + 1)]);
+            const bf16x4 *v = va[j % (PF + 1)];
+            const bf16x8 a = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const int db = j & 15;
+            if (j < 16) {
+                oacc[db] = mfma32x32x16(a, pop0, oacc[db]);
+                if (j < 8) {                    // second half of the probabilities
+                    sacc[8 + j] = fast_exp2(__builtin_fmaf(sacc[8 + j], p.scale_log2, -m_use));
+                }
+                if (j == 8) {
+                    pop1 = to_bf16x8(sacc[8], sacc[9], sacc[10], sacc[11], sacc[12], sacc[13], sacc[14], sacc[15]);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) lsum += sacc[i];
+                }
+            } else {
+                oacc[db] = mfma32x32x16(a, pop1, oacc[db]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         l_run = l_run * alpha + lsum;
-        const bf16x8 pop = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-#pragma unroll
-        for (int db = 0; db < DC / 16; ++db) {
-            const int ch = 2 * db + v_chunk_lane;
-            const bf16x4 lo4 = lds_read_tr16(kt + tile_off(v_row_lane, ch) + v_byte_lane);
-            const bf16x4 hi4 = lds_read_tr16(kt + tile_off(v_row_lane + 16, ch) + v_byte_lane);
-            const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[db] = mfma16x16x32(a, pop, oacc[db]);
-            if ((db & 3) == 3) __builtin_amdgcn_sched_barrier(0);      // bound the load look-ahead
-        }
     }
 
-    float lt = l_run + shfl_xor(l_run, 16);
-    lt += shfl_xor(lt, 32);
+    const float lt = l_run + shfl_xor(l_run, 32);
     if (!head_ok) return;
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const size_t ws = ((size_t)b * p.H + h) * p.n_split_max + s;
     float *wo = p.ws_o + ws * DC;
-    // O^T element i of d-block db is d = 16db + 4*q16 + i of head column j16
+    // O^T element i of d-block db is d = 32db + 8(i/4) + 4hh + (i%4) of head column l32
 #pragma unroll
-    for (int db = 0; db < DC / 16; ++db)
-        *reinterpret_cast<f32x4 *>(wo + 16 * db + 4 * q16) = oacc[db] * inv;
-    if (q16 == 0) p.ws_lse[ws] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
+    for (int db = 0; db < DC / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            f32x4 v = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                       oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
+            *reinterpret_cast<f32x4 *>(wo + 32 * db + 8 * g + 4 * hh) = v;
+        }
+    if (hh == 0) p.ws_lse[ws] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
 }
 
 }  // namespace
@@ -228,6 +362,7 @@ hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream) {
     p.seq_lens = a.seq_lens;
     p.ws_o = a.ws_o;
     p.ws_lse = a.ws_lse;
+    p.B = a.B;
     p.S_max = a.S_max;
     p.H = a.H;
     p.split = a.split;
@@ -240,9 +375,10 @@ hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int n_hchunk = (a.H + HPC - 1) / HPC;
-    dim3 grid(a.n_split_max, n_hchunk, a.B);
-    hipLaunchKernelGGL(mla_decode_kernel, grid, dim3(64 * NW), LDS_BYTES, stream, p);
+    p.n_hchunk = (a.H + HPC - 1) / HPC;
+    const long long n_wg = (long long)a.B * a.n_split_max * p.n_hchunk;
+    if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)n_wg), dim3(64 * NW), LDS_BYTES, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_combine(a.ws_o, a.ws_lse, a.seq_lens, a.o, a.lse, a.B, a.H, DC, a.S_max,
