@@ -38,6 +38,77 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Score-product MFMAs as inline asm with a VGPR accumulator, for kernels
+// whose output accumulators fill the AGPRs (the compiler would otherwise
+// place every MFMA accumulator there and spill).  The hazards the compiler
+// cannot see through asm are covered here: the first MFMA of a chain waits
+// 5 cycles (VALU writes of its operands just before), consecutive MFMAs of
+// one chain accumulate into the same registers with the same opcode
+// (forwarded by the hardware), and mfma_s_last is followed by 19 wait states
+// before any VALU instruction may read the 16-pass result.  Operands coming
+// from LDS or global loads are covered by the waitcnts the compiler inserts
+// for every asm register operand.  Callers put a sched_barrier after the
+// last MFMA of a group of chains so that no read of any of them is scheduled
+// before the trailing wait states.
+__device__ __forceinline__ f32x16 mfma_s_first(bf16x8 a, bf16x8 b) {
+    f32x16 d;
+    asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+__device__ __forceinline__ f32x16 mfma_s_acc(bf16x8 a, bf16x8 b, f32x16 c) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+    return c;
+}
+__device__ __forceinline__ f32x16 mfma_s_last(bf16x8 a, bf16x8 b, f32x16 c) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
+        : "+v"(c) : "v"(a), "v"(b));
+    return c;
+}
+// Output-product MFMA as inline asm with the accumulator pinned in AGPRs.
+// Its B operand must have been written by VALU at least 5 wait states
+// earlier (the callers' operands are older than the preceding mfma_s_last).
+__device__ __forceinline__ void mfma_o_acc(bf16x8 a, bf16x8 b, f32x16 &acc) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// 19 wait states after the last MFMA that wrote `acc` (AGPRs), before VALU
+// reads of it; ties the accumulator so that no read is scheduled earlier.
+__device__ __forceinline__ void settle_acc(f32x16 &acc) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+a"(acc));
+}
+// acc *= f on an accumulator held in AGPRs, as asm so that a (rare)
+// conditional rescale does not make the compiler move the output registers
+// through VGPRs around the branch.  The leading wait states cover an MFMA
+// that may have written the accumulator just before; the trailing ones cover
+// the AGPR writes before the next MFMA reads them as its accumulator.
+__device__ __forceinline__ void scale_acc(f32x16 &acc, float f) {
+    float t;
+    asm volatile(
+        "s_nop 7\n\ts_nop 7\n\ts_nop 4\n\t"
+        "v_accvgpr_read_b32 %[t], %[a0]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a0], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a1]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a1], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a2]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a2], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a3]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a3], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a4]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a4], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a5]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a5], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a6]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a6], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a7]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a7], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a8]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a8], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a9]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a9], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a10]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a10], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a11]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a11], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a12]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a12], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a13]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a13], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a14]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a14], %[t]\n\t"
+        "v_accvgpr_read_b32 %[t], %[a15]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a15], %[t]\n\t"
+        "s_nop 4"
+        : [a0] "+a"(acc[0]), [a1] "+a"(acc[1]), [a2] "+a"(acc[2]), [a3] "+a"(acc[3]),
+          [a4] "+a"(acc[4]), [a5] "+a"(acc[5]), [a6] "+a"(acc[6]), [a7] "+a"(acc[7]),
+          [a8] "+a"(acc[8]), [a9] "+a"(acc[9]), [a10] "+a"(acc[10]), [a11] "+a"(acc[11]),
+          [a12] "+a"(acc[12]), [a13] "+a"(acc[13]), [a14] "+a"(acc[14]), [a15] "+a"(acc[15]),
+          [t] "=&v"(t)
+        : [f] "v"(f));
+}
+
 // Two fp32 -> packed bf16x2 with round-to-nearest-even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     f32x2 v = {lo, hi};
@@ -57,11 +128,36 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + the sum of the eight bf16 values of v (v_dot2_f32_bf16 against (1, 1):
+// two values per instruction; bf16 values times 1 are exact).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+    return acc;
+}
+
 // Value of lane (l ^ mask), through ds_bpermute (any mask < 64).
 __device__ __forceinline__ float shfl_xor(float x, int mask) {
     int lane = __lane_id();
     int src = lane ^ mask;
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
+// Max / sum of x over the lane pair (l, l ^ 32) through v_permlane32_swap
+// (a VALU exchange of the two wave halves; lane l receives x[l % 32] and
+// x[l % 32 + 32]).  Both lanes of a pair get bitwise the same result.
+__device__ __forceinline__ float pair32_max(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding:
@@ -154,6 +250,12 @@ __device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base) {
 // byte offset (the saddr form: one VGPR per address instead of two).
 __device__ __forceinline__ void dma16_off(const void *gbase, uint32_t off, const void *lds_base) {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_offset(lds_base));
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(gbase), "s"(m0v) : "memory");
+}
+// The same with the LDS destination given as a wave-uniform LDS byte address.
+__device__ __forceinline__ void dma16_off_at(const void *gbase, uint32_t off, uint32_t lds_addr_u) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr_u);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(off), "s"(gbase), "s"(m0v) : "memory");
 }

@@ -74,61 +74,6 @@ struct Params {
 // in the loop indices.
 __device__ __forceinline__ int row_slot(int r) { return LROW_SLOTS * r + ((r >> 2) & 3); }
 
-// The score product as inline asm with a VGPR accumulator.  Hazards the
-// compiler cannot see through asm are covered here: the first MFMA of a chain
-// waits 5 cycles (VALU writes of its operands just before), consecutive
-// MFMAs of one chain accumulate into the same registers with the same opcode
-// (forwarded by the hardware), and the last one is followed by 19 wait states
-// before any VALU instruction may read the 16-pass result.  Operands coming
-// from LDS or global loads are covered by the waitcnts the compiler inserts
-// for every asm register operand.
-__device__ __forceinline__ f32x16 mfma_s_first(bf16x8 a, bf16x8 b) {
-    f32x16 d;
-    asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
-    return d;
-}
-__device__ __forceinline__ f32x16 mfma_s_acc(bf16x8 a, bf16x8 b, f32x16 c) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-    return c;
-}
-__device__ __forceinline__ f32x16 mfma_s_last(bf16x8 a, bf16x8 b, f32x16 c) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
-                 : "+v"(c) : "v"(a), "v"(b));
-    return c;
-}
-
-// acc *= f on an accumulator held in AGPRs, as asm so that the (rare)
-// conditional rescale does not make the compiler move the 256 output
-// registers through VGPRs around the branch.  The trailing wait states cover
-// the AGPR writes before the next MFMA reads them as its accumulator.
-__device__ __forceinline__ void scale_acc(f32x16 &acc, float f) {
-    float t;
-    asm volatile(
-        "v_accvgpr_read_b32 %[t], %[a0]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a0], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a1]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a1], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a2]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a2], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a3]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a3], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a4]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a4], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a5]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a5], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a6]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a6], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a7]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a7], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a8]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a8], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a9]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a9], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a10]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a10], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a11]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a11], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a12]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a12], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a13]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a13], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a14]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a14], %[t]\n\t"
-        "v_accvgpr_read_b32 %[t], %[a15]\n\tv_mul_f32 %[t], %[t], %[f]\n\tv_accvgpr_write_b32 %[a15], %[t]\n\t"
-        "s_nop 4"
-        : [a0] "+a"(acc[0]), [a1] "+a"(acc[1]), [a2] "+a"(acc[2]), [a3] "+a"(acc[3]),
-          [a4] "+a"(acc[4]), [a5] "+a"(acc[5]), [a6] "+a"(acc[6]), [a7] "+a"(acc[7]),
-          [a8] "+a"(acc[8]), [a9] "+a"(acc[9]), [a10] "+a"(acc[10]), [a11] "+a"(acc[11]),
-          [a12] "+a"(acc[12]), [a13] "+a"(acc[13]), [a14] "+a"(acc[14]), [a15] "+a"(acc[15]),
-          [t] "=&v"(t)
-        : [f] "v"(f));
-}
-
 __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(Params p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];

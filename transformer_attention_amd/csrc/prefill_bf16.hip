@@ -27,11 +27,12 @@
 //    transposing LDS load ds_read_b64_tr_b16 (two per operand), whose four
 //    source rows are exactly the four keys each lane's P values belong to;
 //  * K and V tiles (64 keys) are stored row-major in LDS with padded rows so
-//    every LDS address stays base + immediate: rows are 304 bytes apart (19
-//    16-byte slots, 19 = 3 mod 16), so the 16 consecutive rows of one column
-//    that the K reads touch hit 16 distinct slots; the transposing V reads
-//    share the stride (a 320-byte V stride, conflict-free for them, measured
-//    slower overall because it costs LDS capacity and ring depth);
+//    every LDS address stays base + immediate and no read has bank
+//    conflicts: K rows are 304 bytes apart (19 16-byte slots, 19 = 3 mod 16:
+//    the 16 consecutive rows of one column that a quarter wave reads hit 16
+//    distinct slots), V rows 320 bytes apart (20 = 4 mod 16: the 4 rows x 64
+//    bytes that a half wave reads through the transposing load fill the 16
+//    slots exactly once);
 //  * K/V tiles stream HBM -> LDS through a 4-stage ring filled by
 //    global_load_lds_dwordx4 (no staging registers): while a wave computes
 //    the scores of tile t+1 and the P.V product of tile t, tiles t+2 and t+3
@@ -56,7 +57,7 @@ namespace {
 
 constexpr int D = 128;          // head size
 constexpr int ROWB = D * 2 + 48;   // LDS row stride of a K row (304 B = 19 slots)
-constexpr int VROWB = D * 2 + 48;  // LDS row stride of a V row
+constexpr int VROWB = D * 2 + 64;  // LDS row stride of a V row (320 B = 20 slots)
 constexpr int LDS_BUDGET = 160 * 1024;
 constexpr int WG_ROWS = 256;    // query rows x heads per workgroup
 constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
     constexpr int RW = 32 * NB;     // query rows per wave
     constexpr int BN = 32 * KB;     // keys per tile
     constexpr int KTILE_BYTES = BN * ROWB;
-    constexpr int STAGE_BYTES = (2 * BN * ROWB + 1023) / 1024 * 1024;   // K rows, V rows
+    constexpr int STAGE_BYTES = (BN * (ROWB + VROWB) + 1023) / 1024 * 1024;   // K rows, V rows
     constexpr int AHEAD = NSTAGE - 1;                                  // tiles issued ahead
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x;
@@ -173,45 +174,84 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
     // (their scores are masked, their P is 0).
     constexpr int NBLK = STAGE_BYTES / 1024;
     constexpr int PER_WAVE = (NBLK + NW - 1) / NW;
-    const int my_blk0 = PER_WAVE * wave;
-    const int my_nblk = min(PER_WAVE, NBLK - PER_WAVE * wave);
-    auto issue_tile = [&](int t) {
-        char *stage = smem + ((t - t_begin) % NSTAGE) * STAGE_BYTES;
-        const int ts = t * BN;
+    // Every wave issues exactly PER_WAVE one-KB copies per tile (the last
+    // wave repeats its final block where the stage has fewer blocks: the
+    // repeat writes the same bytes to the same place), so the wait counts
+    // below are compile-time constants.  Per block: the byte offset inside
+    // the tile's K (or V) rows, computed once; the tile's base address is
+    // wave-uniform and goes in SGPRs.
+    uint32_t dma_off[PER_WAVE];
+    int dma_row[PER_WAVE];
+    bool dma_is_v[PER_WAVE];
 #pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            if (i >= my_nblk) break;
-            const int blk = my_blk0 + i;
-            const int o = blk * 1024 + lane * 16;
-            const bool is_v = o >= KTILE_BYTES;
-            const int ro = is_v ? o - KTILE_BYTES : o;
-            const int r = min(is_v ? ro / VROWB : ro / ROWB, BN - 1);   // constant divisors
-            const int ch = min((ro - r * (is_v ? VROWB : ROWB)) >> 4, D / 8 - 1);
-            const int key = min(ts + r, T - 1);
-            dma16((is_v ? vg : kg) + (size_t)key * D + 8 * ch, stage + blk * 1024);
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int blk = min(PER_WAVE * wave + i, NBLK - 1);
+        const int o = blk * 1024 + lane * 16;
+        dma_is_v[i] = blk * 1024 >= KTILE_BYTES;      // wave-uniform (a block never straddles)
+        const int ro = dma_is_v[i] ? o - KTILE_BYTES : o;
+        const int stride = dma_is_v[i] ? VROWB : ROWB;
+        const int r = min(ro / stride, BN - 1);
+        const int ch = min((ro - r * stride) >> 4, D / 8 - 1);
+        dma_row[i] = r;
+        dma_off[i] = (uint32_t)(r * D * 2 + ch * 16);
+    }
+    const uint32_t smem_lds = lds_offset(smem);
+    auto issue_tile = [&](int t) {
+        const uint32_t stage = smem_lds + ((t - t_begin) % NSTAGE) * STAGE_BYTES;
+        const int ts = t * BN;
+        const __bf16 *kb0 = kg + (size_t)ts * D;
+        const __bf16 *vb0 = vg + (size_t)ts * D;
+        if (ts + BN <= T) {
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i)
+                dma16_off_at(dma_is_v[i] ? vb0 : kb0, dma_off[i],
+                             stage + min(PER_WAVE * wave + i, NBLK - 1) * 1024);
+        } else {                                      // ragged last tile: rows past T re-read row T-1
+            const int last = T - 1 - ts;
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) {
+                const uint32_t off = dma_row[i] > last
+                    ? dma_off[i] - (uint32_t)((dma_row[i] - last) * D * 2) : dma_off[i];
+                dma16_off_at(dma_is_v[i] ? vb0 : kb0, off, stage + min(PER_WAVE * wave + i, NBLK - 1) * 1024);
+            }
         }
     };
+    static_assert(AHEAD <= 4, "wait counts below assume at most 4 tiles in flight");
     auto wait_tiles = [&](int newer) {       // all but the `newer` most recent tiles landed
-        wait_vmcnt_dyn(newer <= 0 ? 0 : newer * my_nblk);
+        if (newer >= 3) wait_vmcnt<3 * PER_WAVE>();
+        else if (newer == 2) wait_vmcnt<2 * PER_WAVE>();
+        else if (newer == 1) wait_vmcnt<PER_WAVE>();
+        else wait_vmcnt<0>();
     };
 
     // S^T = K Q^T for one tile: s[nb][kb] holds keys 32kb + 8(i/4) + 4hi + (i%4)
     // of row row0 + 32nb.
+    // With 64 rows per wave the output accumulators fill the AGPRs and the
+    // score MFMAs go through asm with VGPR accumulators (see mfma_s_first).
+    constexpr bool ASM_S = NB >= 2;
+    auto smfma = [&](int ks, int kb, int nb, bf16x8 a, f32x16 &acc) {
+        if constexpr (ASM_S) {
+            if (ks == 0) acc = mfma_s_first(a, qop[nb][0]);
+            else if (ks == 7 && kb == KB - 1 && nb == NB - 1) acc = mfma_s_last(a, qop[nb][7], acc);
+            else acc = mfma_s_acc(a, qop[nb][ks], acc);
+        } else {
+            if (ks == 0) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+            }
+            acc = mfma32x32x16(a, qop[nb][ks], acc);
+        }
+    };
     auto qk = [&](const char *kt, f32x16 (&s)[NB][KB]) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[nb][kb][i] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + tile_off(32 * kb + l32, 2 * ks + hi));
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) s[nb][kb] = mfma32x32x16(a, qop[nb][ks], s[nb][kb]);
+                for (int nb = 0; nb < NB; ++nb) smfma(ks, kb, nb, a, s[nb][kb]);
             }
+        if constexpr (ASM_S) __builtin_amdgcn_sched_barrier(0);
     };
     // Mask tile t in place (raw scores -> -inf where the key is not visible).
     // Element (kb, i) is key ts + 4hi + e with e = 32kb + 8(i/4) + (i%4).
@@ -240,8 +280,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        return mx * c;
+        return pair32_max(mx) * c;
     };
     // V^T operand for (db, kb, half): two transposing reads of rows
     // 32kb + 16half + 4hi + (j16>>2) (+8), d = 32db + 16(q16&1) + 4(j16&3) .. +3.
@@ -256,15 +295,16 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
         return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     // Probabilities of key block kb (16 values) -> two bf16x8 B operands; adds to lsum.
+    // The row sum adds the bf16-rounded probabilities (two per v_dot2 with
+    // (1, 1)): the same weights the P.V product uses.
     auto probs = [&](const f32x16 &s, float m_use, float &lsum, bf16x8 &p0, bf16x8 &p1) {
         float pv[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            pv[i] = fast_exp2(__builtin_fmaf(s[i], c, -m_use));
-            lsum += pv[i];
-        }
+        for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(s[i], c, -m_use));
         p0 = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
         p1 = to_bf16x8(pv[8], pv[9], pv[10], pv[11], pv[12], pv[13], pv[14], pv[15]);
+        lsum = sum_bf16x8(p0, lsum);
+        lsum = sum_bf16x8(p1, lsum);
     };
 
     // ---- prologue: tiles tb .. tb+AHEAD-1 in flight; S(tb) and its max ----
@@ -313,7 +353,10 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                    for (int db = 0; db < 4; ++db) oacc[nb][db] *= alpha[nb];
+                    for (int db = 0; db < 4; ++db) {
+                        if constexpr (ASM_S) scale_acc(oacc[nb][db], alpha[nb]);
+                        else oacc[nb][db] *= alpha[nb];
+                    }
             }
         }
 
@@ -324,20 +367,14 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
             float lsum[NB];
             bf16x8 pop[NB][KB][2];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                lsum[nb] = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) s_nxt[nb][kb][i] = 0.f;
-            }
+            for (int nb = 0; nb < NB; ++nb) lsum[nb] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
                     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kn + tile_off(32 * kb + l32, 2 * ks + hi));
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) s_nxt[nb][kb] = mfma32x32x16(a, qop[nb][ks], s_nxt[nb][kb]);
+                    for (int nb = 0; nb < NB; ++nb) smfma(ks, kb, nb, a, s_nxt[nb][kb]);
                 }
                 // spread the NB*KB probability blocks over the 8 MFMA steps
 #pragma unroll
@@ -347,6 +384,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
                         if (ks == 1 + (6 * (nb * KB + kb)) / (NB * KB))
                             probs(s_cur[nb][kb], m_use[nb], lsum[nb], pop[nb][kb][0], pop[nb][kb][1]);
             }
+            if constexpr (ASM_S) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) l_run[nb] += lsum[nb];
 #pragma unroll
@@ -357,8 +395,10 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
                     for (int db = 0; db < 4; ++db) {
                         const bf16x8 a = v_operand(vc, db, kb, half);
 #pragma unroll
-                        for (int nb = 0; nb < NB; ++nb)
-                            oacc[nb][db] = mfma32x32x16(a, pop[nb][kb][half], oacc[nb][db]);
+                        for (int nb = 0; nb < NB; ++nb) {
+                            if constexpr (ASM_S) mfma_o_acc(a, pop[nb][kb][half], oacc[nb][db]);
+                            else oacc[nb][db] = mfma32x32x16(a, pop[nb][kb][half], oacc[nb][db]);
+                        }
                     }
         } else if (act_n) {
             qk(kn, s_nxt);
@@ -381,11 +421,17 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
     if (t < t_end) iteration(t, sa, sb);
 
     if (!wave_active) return;
+    if constexpr (ASM_S) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) settle_acc(oacc[nb][db]);
+    }
     // Epilogue: O = O~ / l, L = m ln2 + ln l.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int row = row0 + 32 * nb;
-        const float lt = l_run[nb] + shfl_xor(l_run[nb], 32);
+        const float lt = pair32_sum(l_run[nb]);
         if (row >= T) continue;
         const float inv = lt > 0.f ? 1.0f / lt : 0.f;
         __bf16 *orow = p.o + q_base + (size_t)row * D;
@@ -420,7 +466,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
 hipError_t launch_prefill_bf16_d128(const PrefillArgs &a, hipStream_t stream) {
     constexpr int NB = PREFILL_NB, KB = PREFILL_KB, NST = PREFILL_NSTAGE;
     constexpr int NW = 8 / NB;
-    constexpr int LDS_BYTES = NST * ((2 * 32 * KB * ROWB + 1023) / 1024 * 1024);
+    constexpr int LDS_BYTES = NST * ((32 * KB * (ROWB + VROWB) + 1023) / 1024 * 1024);
     static_assert(LDS_BYTES <= LDS_BUDGET, "LDS ring too large");
     Params p;
     p.q = static_cast<const __bf16 *>(a.q);
