@@ -62,6 +62,16 @@ constexpr int LDS_BUDGET = 160 * 1024;
 constexpr int WG_ROWS = 256;    // query rows x heads per workgroup
 constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
 
+#ifndef PREFILL_NB
+#define PREFILL_NB 1
+#endif
+#ifndef PREFILL_KB
+#define PREFILL_KB 2
+#endif
+#ifndef PREFILL_NSTAGE
+#define PREFILL_NSTAGE 4
+#endif
+
 struct Params {
     const __bf16 *q, *k, *v;
     __bf16 *o;
@@ -328,7 +338,9 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
         const int rel = t - t_begin;
         wait_tiles(min(AHEAD - 2, t_end - t - 2));    // tile t+1 landed
         raw_barrier();                                // iteration t-1 done everywhere
-        if (t + AHEAD < t_end) issue_tile(t + AHEAD); // into the stage of tile t-1
+        // the copy of tile t+AHEAD (into the stage of tile t-1) is issued
+        // between the first score MFMAs when this wave has a tile to compute
+        const bool dma_now = t + AHEAD < t_end;
 
         const bool act_c = tile_active(t);
         const bool act_n = tile_active(t + 1);
@@ -368,14 +380,27 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
             bf16x8 pop[NB][KB][2];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) lsum[nb] = 0.f;
+            // K operands are loaded KPF k-steps ahead of their MFMAs
+            constexpr int KPF = 2;
+            bf16x8 ka[KPF + 1][KB];
+#pragma unroll
+            for (int i = 0; i < KPF; ++i)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    ka[i][kb] = *reinterpret_cast<const bf16x8 *>(kn + tile_off(32 * kb + l32, 2 * i + hi));
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
+                if (ks + KPF < 8) {
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kn + tile_off(32 * kb + l32, 2 * ks + hi));
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) smfma(ks, kb, nb, a, s_nxt[nb][kb]);
+                    for (int kb = 0; kb < KB; ++kb)
+                        ka[(ks + KPF) % (KPF + 1)][kb] =
+                            *reinterpret_cast<const bf16x8 *>(kn + tile_off(32 * kb + l32, 2 * (ks + KPF) + hi));
                 }
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) smfma(ks, kb, nb, ka[ks % (KPF + 1)][kb], s_nxt[nb][kb]);
+                if (ks == 1 && dma_now) issue_tile(t + AHEAD);
                 // spread the NB*KB probability blocks over the 8 MFMA steps
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
@@ -383,33 +408,55 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
                     for (int kb = 0; kb < KB; ++kb)
                         if (ks == 1 + (6 * (nb * KB + kb)) / (NB * KB))
                             probs(s_cur[nb][kb], m_use[nb], lsum[nb], pop[nb][kb][0], pop[nb][kb][1]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (ASM_S) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) l_run[nb] += lsum[nb];
+            // row max of tile t+1, spread over the P.V MFMAs below
+            if (act_n && tile_needs_mask(t + 1)) apply_mask(t + 1, s_nxt);
+            float mpart[NB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int nb = 0; nb < NB; ++nb) mpart[nb] = -INFINITY;
+            // V operands are loaded VPF MFMA steps ahead
+            constexpr int NV = KB * 2 * 4;            // (kb, half, db) steps
+            constexpr int VPF = 3;
+            bf16x8 va[VPF + 1];
+            auto vop = [&](int j) { return v_operand(vc, j & 3, j >> 3, (j >> 2) & 1); };
 #pragma unroll
-                for (int half = 0; half < 2; ++half)
+            for (int i = 0; i < VPF; ++i) va[i] = vop(i);
 #pragma unroll
-                    for (int db = 0; db < 4; ++db) {
-                        const bf16x8 a = v_operand(vc, db, kb, half);
+            for (int j = 0; j < NV; ++j) {
+                if (j + VPF < NV) va[(j + VPF) % (VPF + 1)] = vop(j + VPF);
+                const int db = j & 3, kb = j >> 3, half = (j >> 2) & 1;
 #pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) {
-                            if constexpr (ASM_S) mfma_o_acc(a, pop[nb][kb][half], oacc[nb][db]);
-                            else oacc[nb][db] = mfma32x32x16(a, pop[nb][kb][half], oacc[nb][db]);
-                        }
-                    }
-        } else if (act_n) {
-            qk(kn, s_nxt);
-        }
-        if (act_n) {
-            if (tile_needs_mask(t + 1)) apply_mask(t + 1, s_nxt);
+                for (int nb = 0; nb < NB; ++nb) {
+                    if constexpr (ASM_S) mfma_o_acc(va[j % (VPF + 1)], pop[nb][kb][half], oacc[nb][db]);
+                    else oacc[nb][db] = mfma32x32x16(va[j % (VPF + 1)], pop[nb][kb][half], oacc[nb][db]);
+                }
+                // 8 scores of s_nxt per step for the first NB*KB*2 steps
+                if (j < 2 * NB * KB) {
+                    const int nb = j / (2 * KB), kb = (j / 2) % KB, h8 = 8 * (j & 1);
+                    float m8 = fmaxf(fmaxf(fmaxf(s_nxt[nb][kb][h8], s_nxt[nb][kb][h8 + 1]),
+                                           fmaxf(s_nxt[nb][kb][h8 + 2], s_nxt[nb][kb][h8 + 3])),
+                                     fmaxf(fmaxf(s_nxt[nb][kb][h8 + 4], s_nxt[nb][kb][h8 + 5]),
+                                           fmaxf(s_nxt[nb][kb][h8 + 6], s_nxt[nb][kb][h8 + 7])));
+                    mpart[nb] = fmaxf(mpart[nb], m8);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = tile_max(s_nxt[nb]);
+            for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = act_n ? pair32_max(mpart[nb]) * c : -INFINITY;
         } else {
+            if (dma_now) issue_tile(t + AHEAD);
+            if (act_n) {
+                qk(kn, s_nxt);
+                if (tile_needs_mask(t + 1)) apply_mask(t + 1, s_nxt);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = -INFINITY;
+                for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = tile_max(s_nxt[nb]);
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = -INFINITY;
+            }
         }
     };
 
@@ -451,15 +498,6 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
     }
 }
 
-#ifndef PREFILL_NB
-#define PREFILL_NB 1
-#endif
-#ifndef PREFILL_KB
-#define PREFILL_KB 2
-#endif
-#ifndef PREFILL_NSTAGE
-#define PREFILL_NSTAGE 4
-#endif
 
 }  // namespace
 
