@@ -42,14 +42,24 @@ namespace {
 
 constexpr int D = 128;
 constexpr int BN = 32;                    // keys per tile
-constexpr int NW = 4;                     // waves per workgroup (independent)
+#ifndef DECODE_NW
+#define DECODE_NW 4
+#endif
+#ifndef DECODE_NSTG
+#define DECODE_NSTG 2
+#endif
+constexpr int NW = DECODE_NW;             // waves per workgroup (independent)
+constexpr int NSTG = DECODE_NSTG;         // stages of each wave's private ring
 constexpr int KROW = D * 2 + 16;          // 272 B
 constexpr int VROW = D * 2 + 32;          // 288 B
-constexpr int KREG = BN * KROW;           // 8704 B
-constexpr int STAGE_BLK = (BN * (KROW + VROW) + 1023) / 1024;   // 18 one-KB blocks
+constexpr int KREG = 9 * 1024;            // K rows (8704 B) padded to whole one-KB DMA blocks, so
+                                          // no block straddles the K and V regions
+constexpr int STAGE_BLK = (KREG + BN * VROW + 1023) / 1024;      // 18 one-KB blocks
 constexpr int STAGE_BYTES = STAGE_BLK * 1024;                   // 18432 B
-constexpr int WAVE_BYTES = 2 * STAGE_BYTES;                     // private ring
-constexpr int LDS_BYTES = NW * WAVE_BYTES;                      // 147456 B
+constexpr int WAVE_BYTES = NSTG * STAGE_BYTES;                  // private ring
+constexpr int LDS_BYTES = NW * WAVE_BYTES;
+static_assert(LDS_BYTES <= 160 * 1024, "decode rings exceed the LDS");
+static_assert(NSTG >= 2 && NSTG <= 4, "the wait below handles up to 3 tiles in flight");
 constexpr float TAU = 8.0f;
 
 struct Params {
@@ -133,21 +143,24 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
 
     // Per-lane DMA offsets inside a tile: block i of a stage covers stage
     // bytes [1024 i, 1024 i + 1024); lane byte o = 1024 i + 16 lane holds K row
-    // o / 272 (o < 8704) or V row (o - 8704) / 288, chunk (remainder) / 16
-    // (pad slots and bytes past the last row take a valid chunk of the last
-    // row).
-    int rel_row[STAGE_BLK], col_off[STAGE_BLK];
+    // o / 272 (o < 9216; rows past 31 and pad slots take a valid chunk of the
+    // last row) or V row (o - 9216) / 288, chunk (remainder) / 16.
+    // The byte offset of each block's lane chunk relative to the tile's
+    // first K (or V) row is fixed; only the ragged last tile of a unit needs
+    // its rows clamped.
+    uint32_t blk_off[STAGE_BLK];
     unsigned is_v_mask = 0;
 #pragma unroll
     for (int i = 0; i < STAGE_BLK; ++i) {
         const int o = i * 1024 + lane * 16;
-        const bool is_v = o >= KREG;
+        const bool is_v = i * 1024 >= KREG;         // wave-uniform: blocks never straddle K and V
         const int ro = is_v ? o - KREG : o;
         const int r = min(is_v ? ro / VROW : ro / KROW, BN - 1);
-        rel_row[i] = r;
-        col_off[i] = min((ro - r * (is_v ? VROW : KROW)) >> 4, D / 8 - 1) * 16;
+        const int col = min((ro - r * (is_v ? VROW : KROW)) >> 4, D / 8 - 1) * 16;
+        blk_off[i] = (uint32_t)(r * D * 2 + col);
         is_v_mask |= (unsigned)is_v << i;
     }
+    const uint32_t ring_lds = lds_offset(ring);
 
     // Fetch cursor: unit id fu (geometry fd), tile ft; fetched-tile counter nf.
     int fu = wid, ft = 0, nf = 0, f_walk = 0;
@@ -164,15 +177,22 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         fetch_skip_empty();
         if (fu >= total) return false;
         const size_t kv_base = ((size_t)fd.b * p.hkv + fd.g) * (size_t)p.S_max * D;
-        const char *kg = reinterpret_cast<const char *>(p.k + kv_base);
-        const char *vg = reinterpret_cast<const char *>(p.v + kv_base);
         const int t0 = fd.lo + ft * BN;
-        char *stage = ring + (nf & 1) * STAGE_BYTES;
+        const char *kg = reinterpret_cast<const char *>(p.k + kv_base + (size_t)t0 * D);
+        const char *vg = reinterpret_cast<const char *>(p.v + kv_base + (size_t)t0 * D);
+        const uint32_t stage = ring_lds + (nf % NSTG) * STAGE_BYTES;
+        if (t0 + BN <= fd.hi) {
 #pragma unroll
-        for (int i = 0; i < STAGE_BLK; ++i) {
-            const int key = min(t0 + rel_row[i], fd.hi - 1);
-            const char *base = ((is_v_mask >> i) & 1) ? vg : kg;
-            dma16(base + (size_t)key * (D * 2) + col_off[i], stage + i * 1024);
+            for (int i = 0; i < STAGE_BLK; ++i)
+                dma16_off_at(((is_v_mask >> i) & 1) ? vg : kg, blk_off[i], stage + i * 1024);
+        } else {                                   // ragged tile: rows past the end re-read the last row
+            const uint32_t lim = (uint32_t)(fd.hi - 1 - t0) * (D * 2);
+#pragma unroll
+            for (int i = 0; i < STAGE_BLK; ++i) {
+                const uint32_t row_b = blk_off[i] & ~(uint32_t)(D * 2 - 1);
+                const uint32_t off = row_b > lim ? lim + (blk_off[i] & (D * 2 - 1)) : blk_off[i];
+                dma16_off_at(((is_v_mask >> i) & 1) ? vg : kg, off, stage + i * 1024);
+            }
         }
         ++ft;
         ++nf;
@@ -185,8 +205,10 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
     const int k_lane_off = j16 * KROW + q16 * 16;
 
     // Prime the ring.
-    bool more = issue_next();
-    if (more) issue_next();
+    bool more = true;
+#pragma unroll
+    for (int i = 0; i < NSTG; ++i)
+        if (more) more = issue_next();
     int nc_done = 0;                                  // tiles consumed so far
 
     int c_walk = 0;
@@ -209,19 +231,35 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
 
         for (int j = 0; j < d.n_tiles; ++j) {
             // this tile is the nc_done-th fetched; a later one may be in flight
-            if (nf > nc_done + 1) wait_vmcnt<STAGE_BLK>(); else wait_vmcnt<0>();
-            const char *st = ring + (nc_done & 1) * STAGE_BYTES;
+            {
+                const int newer = nf - nc_done - 1;       // tiles fetched after this one
+                if (NSTG >= 4 && newer >= 3) wait_vmcnt<(NSTG >= 4 ? 3 : 0) * STAGE_BLK>();
+                else if (NSTG >= 3 && newer >= 2) wait_vmcnt<(NSTG >= 3 ? 2 : 0) * STAGE_BLK>();
+                else if (newer >= 1) wait_vmcnt<STAGE_BLK>();
+                else wait_vmcnt<0>();
+            }
+            const char *st = ring + (nc_done % NSTG) * STAGE_BYTES;
             const int t0 = d.lo + j * BN;
+            bf16x8 ka[2][4];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    ka[mb][ks] = *reinterpret_cast<const bf16x8 *>(st + k_lane_off + 16 * mb * KROW + 64 * ks);
+            bf16x4 va[8][2];
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                va[db][0] = lds_read_tr16(st + v_lane_off + 32 * db);
+                va[db][1] = lds_read_tr16(st + v_lane_off + 16 * VROW + 32 * db);
+            }
             f32x4 sacc[2];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(st + k_lane_off + 16 * mb * KROW + 64 * ks);
-                    sacc[mb] = mfma16x16x32(a, qop[ks], sacc[mb]);
+                for (int mb = 0; mb < 2; ++mb) {
+                    if (ks == 0) sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    sacc[mb] = mfma16x16x32(ka[mb][ks], qop[ks], sacc[mb]);
                 }
-            }
             // element (mb, i) of this lane is key t0 + 16 mb + 4 q16 + i of head column j16
             const bool tail = t0 + BN > d.hi;
             float x[8];
@@ -236,7 +274,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
                     mx = fmaxf(mx, v);
                 }
             mx = fmaxf(mx, shfl_xor(mx, 16));
-            mx = fmaxf(mx, shfl_xor(mx, 32));
+            mx = pair32_max(mx);
             const bool upd = mx > m_run + TAU;
             const float m_new = upd ? mx : m_run;
             const float alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
@@ -257,9 +295,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
             const bf16x8 pop = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const bf16x4 lo4 = lds_read_tr16(st + v_lane_off + 32 * db);
-                const bf16x4 hi4 = lds_read_tr16(st + v_lane_off + 16 * VROW + 32 * db);
-                const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                const bf16x8 a = __builtin_shufflevector(va[db][0], va[db][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 oacc[db] = mfma16x16x32(a, pop, oacc[db]);
             }
             ++nc_done;
@@ -270,7 +306,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         }
         // the unit's partial result (an empty unit writes O = 0, L = -inf)
         float lt = l_run + shfl_xor(l_run, 16);
-        lt += shfl_xor(lt, 32);
+        lt = pair32_sum(lt);
         if (head_ok) {
             const float inv = lt > 0.f ? 1.0f / lt : 0.f;
             const size_t ws = (((size_t)d.b * p.hq + h) * p.n_split_max + d.c);
