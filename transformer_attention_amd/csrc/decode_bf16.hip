@@ -57,7 +57,8 @@ constexpr int KREG = 9 * 1024;            // K rows (8704 B) padded to whole one
 constexpr int STAGE_BLK = (KREG + BN * VROW + 1023) / 1024;      // 18 one-KB blocks
 constexpr int STAGE_BYTES = STAGE_BLK * 1024;                   // 18432 B
 constexpr int WAVE_BYTES = NSTG * STAGE_BYTES;                  // private ring
-constexpr int LDS_BYTES = NW * WAVE_BYTES;
+constexpr int QBUF_BYTES = 16 * D * 2;                          // one unit's 16 query rows
+constexpr int LDS_BYTES = NW * (WAVE_BYTES + QBUF_BYTES);
 static_assert(LDS_BYTES <= 160 * 1024, "decode rings exceed the LDS");
 static_assert(NSTG >= 2 && NSTG <= 4, "the wait below handles up to 3 tiles in flight");
 constexpr float TAU = 8.0f;
@@ -119,17 +120,32 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
     const int nwaves = gridDim.x * NW;
     const int total = ld_uniform(p.plan, p.B);
     char *ring = smem + wave * WAVE_BYTES;
+    char *qbuf = smem + NW * WAVE_BYTES + wave * QBUF_BYTES;
+    // Every vector-memory instruction of this kernel is issued through asm
+    // (tile copies, query copies, partial stores), and `vmc` counts them, so
+    // each wait below lets exactly the instructions issued after the one
+    // waited for stay in flight (vmcnt drains in issue order).
+    int vmc = 0;
+    auto wait_after = [&](int mark) { wait_vmcnt_dyn(min(vmc - mark, 31)); };   // fewer is stricter
 
     // Unit id -> geometry.  Each cursor visits increasing unit ids, so its
     // sequence index is found by walking forward from its previous one.
     auto describe = [&](int u, int &walk_b) {
-        while (walk_b + 1 < p.B && ld_uniform(p.plan, walk_b + 1) <= u) ++walk_b;
+        // the three scalar loads of a step are issued together (one latency)
+        int pb = ld_uniform(p.plan, walk_b);
+        int pb1 = ld_uniform(p.plan, walk_b + 1);
+        int len = ld_uniform(p.seq_lens, walk_b);
+        while (walk_b + 1 < p.B && pb1 <= u) {
+            ++walk_b;
+            pb = pb1;
+            pb1 = ld_uniform(p.plan, walk_b + 1);
+            len = ld_uniform(p.seq_lens, walk_b);
+        }
         Unit d;
         d.b = walk_b;
-        int len = ld_uniform(p.seq_lens, d.b);
         len = len < 0 ? 0 : (len > p.S_max ? p.S_max : len);
         const int nc = (len + p.split - 1) / p.split;
-        const int r = u - ld_uniform(p.plan, d.b);
+        const int r = u - pb;
         const int gh = r / nc;
         d.c = r - gh * nc;
         d.g = gh / p.n_hchunk;
@@ -162,8 +178,15 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
     }
     const uint32_t ring_lds = lds_offset(ring);
 
-    // Fetch cursor: unit id fu (geometry fd), tile ft; fetched-tile counter nf.
+    // Fetch cursor: unit id fu (geometry fd), tile ft; fetched-tile counter nf;
+    // vm_tile[s] = value of vmc once the tile in ring stage s was issued.
     int fu = wid, ft = 0, nf = 0, f_walk = 0;
+    // With two stages at most two fetched tiles are unconsumed: vm_last /
+    // vm_prev hold vmc after the issue of tile nf-1 / nf-2 (plain scalars: an
+    // indexed array would live in scratch memory, whose accesses are
+    // vector-memory instructions too).
+    static_assert(NSTG == 2, "the issue bookkeeping below tracks two stages");
+    int vm_last = 0, vm_prev = 0;
     Unit fd;
     if (fu < total) fd = describe(fu, f_walk);
     auto fetch_skip_empty = [&]() {
@@ -181,6 +204,9 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         const char *kg = reinterpret_cast<const char *>(p.k + kv_base + (size_t)t0 * D);
         const char *vg = reinterpret_cast<const char *>(p.v + kv_base + (size_t)t0 * D);
         const uint32_t stage = ring_lds + (nf % NSTG) * STAGE_BYTES;
+        vmc += STAGE_BLK;
+        vm_prev = vm_last;
+        vm_last = vmc;
         if (t0 + BN <= fd.hi) {
 #pragma unroll
             for (int i = 0; i < STAGE_BLK; ++i)
@@ -204,6 +230,25 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
     const int v_lane_off = KREG + (4 * q16 + (j16 >> 2)) * VROW + ((j16 & 3) >> 1) * 16 + 8 * (j16 & 1);
     const int k_lane_off = j16 * KROW + q16 * 16;
 
+    // Query rows of a unit: 16 heads x 256 B, contiguous in q, copied into the
+    // wave's query buffer (4 one-KB blocks; rows past the group's heads
+    // re-read its last head and are masked below).
+    const uint32_t qbuf_lds = lds_offset(qbuf);
+    int vm_q = 0, q_walk = 0;
+    auto issue_q = [&](int u) {
+        const Unit e = describe(u, q_walk);
+        const int last = p.G - 1 - e.hc * 16;            // last valid row of the chunk
+        const char *qg = reinterpret_cast<const char *>(p.q + ((size_t)e.b * p.hq + e.g * p.G + e.hc * 16) * D);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = min(4 * i + (lane >> 4), last);
+            dma16_off_at(qg, (uint32_t)(row * D * 2 + (lane & 15) * 16), qbuf_lds + i * 1024);
+        }
+        vmc += 4;
+        vm_q = vmc;
+    };
+    if (wid < total) issue_q(wid);
+
     // Prime the ring.
     bool more = true;
 #pragma unroll
@@ -217,13 +262,18 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         const int hidx = d.hc * 16 + j16;
         const bool head_ok = hidx < p.G;
         const int h = d.g * p.G + hidx;
+        // this unit's query rows (copied one unit ahead) -> B operands
+        wait_after(vm_q);
         bf16x8 qop[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (head_ok) val = ldg16(p.q + ((size_t)d.b * p.hq + h) * D + 32 * ks + 8 * q16);
+            u32x4 val = *reinterpret_cast<const u32x4 *>(qbuf + j16 * D * 2 + (4 * ks + q16) * 16);
+            if (!head_ok) val = u32x4{0u, 0u, 0u, 0u};
             qop[ks] = __builtin_bit_cast(bf16x8, val);
         }
+        asm volatile("" ::: "memory");
+        wait_lgkmcnt0();                              // the buffer may be refilled now
+        if (cu + nwaves < total) issue_q(cu + nwaves);
         f32x4 oacc[8];
 #pragma unroll
         for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -231,13 +281,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
 
         for (int j = 0; j < d.n_tiles; ++j) {
             // this tile is the nc_done-th fetched; a later one may be in flight
-            {
-                const int newer = nf - nc_done - 1;       // tiles fetched after this one
-                if (NSTG >= 4 && newer >= 3) wait_vmcnt<(NSTG >= 4 ? 3 : 0) * STAGE_BLK>();
-                else if (NSTG >= 3 && newer >= 2) wait_vmcnt<(NSTG >= 3 ? 2 : 0) * STAGE_BLK>();
-                else if (newer >= 1) wait_vmcnt<STAGE_BLK>();
-                else wait_vmcnt<0>();
-            }
+            wait_after(nc_done == nf - 1 ? vm_last : vm_prev);   // this tile's copies landed
             const char *st = ring + (nc_done % NSTG) * STAGE_BYTES;
             const int t0 = d.lo + j * BN;
             bf16x8 ka[2][4];
@@ -307,52 +351,96 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         // the unit's partial result (an empty unit writes O = 0, L = -inf)
         float lt = l_run + shfl_xor(l_run, 16);
         lt = pair32_sum(lt);
-        if (head_ok) {
+        // The unit's partial result (asm stores, counted in vmc; lanes of
+        // heads past the group store nothing; the four lanes of a head column
+        // store the same log-sum-exp).
+        {
             const float inv = lt > 0.f ? 1.0f / lt : 0.f;
             const size_t ws = (((size_t)d.b * p.hq + h) * p.n_split_max + d.c);
             float *wo = p.ws_o + ws * D;
+            const float lse2 = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
+            if (head_ok) {
 #pragma unroll
-            for (int db = 0; db < 8; ++db)
-                *reinterpret_cast<f32x4 *>(wo + 16 * db + 4 * q16) = oacc[db] * inv;
-            if (q16 == 0) p.ws_lse[ws] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
+                for (int db = 0; db < 8; ++db) store16(wo + 16 * db + 4 * q16, oacc[db] * inv);
+                store4(p.ws_lse + ws, lse2);
+            }
+            vmc += 9;
         }
     }
     wait_vmcnt<0>();
 }
 
-// One wave per (head, sequence): merge the partials of the sequence's splits.
+// Merge of the split partials: one wave per (sequence, head) row, four rows
+// per workgroup.  Each lane owns DV/64 consecutive output values; the
+// weights 2^(L_s - M) of the splits are computed once per lane (lane s holds
+// split s of a 64-split chunk) and broadcast with readlane, and the partial
+// rows of four splits are loaded before they are accumulated.
 template <int DV>
-__global__ __launch_bounds__(64) void split_combine_kernel(const float *ws_o, const float *ws_lse,
-                                                           const int32_t *seq_lens, __bf16 *o, float *lse,
-                                                           int H, int S_max, int split, int n_split_max) {
-    constexpr int PER = DV / 64;
-    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    int len = seq_lens[b];
+__global__ __launch_bounds__(256) void split_combine_kernel(const float *ws_o, const float *ws_lse,
+                                                            const int32_t *seq_lens, __bf16 *o, float *lse,
+                                                            int n_rows, int H, int S_max, int split,
+                                                            int n_split_max) {
+    constexpr int PER = DV / 64;                  // 2 or 8 values per lane
+    typedef __attribute__((ext_vector_type(PER))) float fvec;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= n_rows) return;
+    const int b = row / H;
+    int len = ld_uniform(seq_lens, b);
     len = len < 0 ? 0 : (len > S_max ? S_max : len);
     const int ns = (len + split - 1) / split;
-    const size_t base = ((size_t)b * H + h) * n_split_max;
+    const float *lrow = ws_lse + (size_t)row * n_split_max;
+    const float *orow = ws_o + (size_t)row * n_split_max * DV + PER * lane;
+
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ws_lse[base + s]);
-    float acc[PER];
+    for (int c0 = 0; c0 < ns; c0 += 64)
+        M = fmaxf(M, c0 + lane < ns ? lrow[c0 + lane] : -INFINITY);
+    M = fmaxf(M, shfl_xor(M, 1));
+    M = fmaxf(M, shfl_xor(M, 2));
+    M = fmaxf(M, shfl_xor(M, 4));
+    M = fmaxf(M, shfl_xor(M, 8));
+    M = fmaxf(M, shfl_xor(M, 16));
+    M = pair32_max(M);
+
+    fvec acc;
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
     float Z = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < ns; ++s) {
-            const float ls = ws_lse[base + s];
-            if (ls == -INFINITY) continue;
-            const float w = fast_exp2(ls - M);
-            Z += w;
-            const float *src = ws_o + (base + s) * DV;
+        for (int c0 = 0; c0 < ns; c0 += 64) {
+            const int cn = min(64, ns - c0);
+            const float w = c0 + lane < ns ? fast_exp2(lrow[c0 + lane] - M) : 0.f;
+            int s = 0;
+            for (; s + 4 <= cn; s += 4) {
+                fvec v[4];
 #pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] += w * src[lane + 64 * i];
+                for (int u = 0; u < 4; ++u)
+                    v[u] = *reinterpret_cast<const fvec *>(orow + (size_t)(c0 + s + u) * DV);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float ws = readlane_f32(w, s + u);
+                    Z += ws;
+                    acc += ws * v[u];
+                }
+            }
+            for (; s < cn; ++s) {
+                const fvec v = *reinterpret_cast<const fvec *>(orow + (size_t)(c0 + s) * DV);
+                const float ws = readlane_f32(w, s);
+                Z += ws;
+                acc += ws * v;
+            }
         }
     }
     const float inv = Z > 0.f ? 1.0f / Z : 0.f;
-    __bf16 *dst = o + ((size_t)b * H + h) * DV;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) dst[lane + 64 * i] = (__bf16)(acc[i] * inv);
-    if (lse && lane == 0) lse[(size_t)b * H + h] = Z > 0.f ? (M + __log2f(Z)) * kLn2 : -INFINITY;
+    __bf16 *dst = o + (size_t)row * DV + PER * lane;
+    if constexpr (PER == 2) {
+        *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+        u32x4 w4 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                    pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+        *reinterpret_cast<u32x4 *>(dst) = w4;
+    }
+    if (lse && lane == 0) lse[row] = Z > 0.f ? (M + __log2f(Z)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -404,16 +492,18 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_split_combine(const float *ws_o, const float *ws_lse, const int32_t *seq_lens,
                                 void *o, float *lse, int B, int H, int dv, int S_max, int split,
                                 int n_split_max, hipStream_t stream) {
-    dim3 grid(H, B);
+    const long long n_rows = (long long)B * H;
+    if (n_rows > 0x7fffffffLL - 4) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((n_rows + 3) / 4));
     __bf16 *ob = static_cast<__bf16 *>(o);
     switch (dv) {
         case 128:
-            hipLaunchKernelGGL(split_combine_kernel<128>, grid, dim3(64), 0, stream, ws_o, ws_lse,
-                               seq_lens, ob, lse, H, S_max, split, n_split_max);
+            hipLaunchKernelGGL(split_combine_kernel<128>, grid, dim3(256), 0, stream, ws_o, ws_lse,
+                               seq_lens, ob, lse, (int)n_rows, H, S_max, split, n_split_max);
             break;
         case 512:
-            hipLaunchKernelGGL(split_combine_kernel<512>, grid, dim3(64), 0, stream, ws_o, ws_lse,
-                               seq_lens, ob, lse, H, S_max, split, n_split_max);
+            hipLaunchKernelGGL(split_combine_kernel<512>, grid, dim3(256), 0, stream, ws_o, ws_lse,
+                               seq_lens, ob, lse, (int)n_rows, H, S_max, split, n_split_max);
             break;
         default: return hipErrorInvalidValue;
     }

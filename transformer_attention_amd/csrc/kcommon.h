@@ -146,6 +146,11 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
+// Value of x in lane `l` (wave-uniform index) for every lane.
+__device__ __forceinline__ float readlane_f32(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
 // Max / sum of x over the lane pair (l, l ^ 32) through v_permlane32_swap
 // (a VALU exchange of the two wave halves; lane l receives x[l % 32] and
 // x[l % 32 + 32]).  Both lanes of a pair get bitwise the same result.
@@ -258,6 +263,17 @@ __device__ __forceinline__ void dma16_off_at(const void *gbase, uint32_t off, ui
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr_u);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(off), "s"(gbase), "s"(m0v) : "memory");
+}
+
+// 16-byte / 4-byte global stores issued through asm, for kernels that count
+// their own vector-memory instructions (the compiler neither counts nor waits
+// for them).  A store reads its data registers when it is issued; the
+// trailing wait state covers a VALU write of them right after.
+__device__ __forceinline__ void store16(void *p, f32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store4(void *p, float v) {
+    asm volatile("global_store_dword %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
 }
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
