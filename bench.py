@@ -9,7 +9,8 @@ also measures the two decode forms on their workloads -- 70B-shaped GQA
 decode (B=64, 64/8 heads, cached lengths uniform in [4096, 32768]) and
 DeepSeek-V3-shaped MLA absorbed decode (B=32, 128 heads, 16384 tokens of
 576 values) -- in KV-cache GB/s, counting only cache rows inside each
-sequence plus q and o.
+sequence plus q and o -- and the two sliding-window prefills (B=4, T=4096,
+32 query heads, window 1024, with 32 and with 1 K/V head) in TFLOP/s.
 
 Inputs are seeded synthetic N(0,1) tensors (workloads.py), resident in HBM
 before timing.  W untimed warm-up steps, then exactly K timed steps between
@@ -205,9 +206,9 @@ def main(argv=None):
         out["prefill"] = bench_prefill(torch, ta, W, shape, args.steps, args.warmup)
         print(f"[bench] prefill {out['prefill']['ms']:.3f} ms "
               f"{out['prefill']['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    if only == "swa-mha":
+    if only in (None, "swa-mha"):
         out["swa_mha"] = bench_prefill(torch, ta, W, W.SWA_MHA, args.steps, args.warmup)
-    if only == "swa-mqa":
+    if only in (None, "swa-mqa"):
         out["swa_mqa"] = bench_prefill(torch, ta, W, W.SWA_MQA, args.steps, args.warmup)
     if only == "copy":
         out["copy"] = bench_copy(torch, args.steps, args.warmup)
@@ -259,6 +260,12 @@ def main(argv=None):
                           "ms": round(d["ms"], 4), "GB_s": round(d["gbs"], 1),
                           "frac_hbm_peak": round(d["frac_hbm_peak"], 4), "bytes": d["bytes"],
                           "sum_len": d["sum_len"]}
+    for key, shp, name in (("swa_mha", W.SWA_MHA, "sliding-window MHA prefill, B=4, T=4096, 32/32 heads, W=1024"),
+                           ("swa_mqa", W.SWA_MQA, "sliding-window MQA prefill, B=4, T=4096, 32/1 heads, W=1024")):
+        if key in out and key != next(iter(out)):
+            r = out[key]
+            line[key] = {"workload": name, "ms": round(r["ms"], 4), "TFLOP_s": round(r["tflops"], 2),
+                         "frac_bf16_peak": round(r["frac_bf16_peak"], 4), "flops": r["flops"]}
     if "mla" in out:
         m = out["mla"]
         line["mla"] = {"workload": "DeepSeek-V3-shaped MLA absorbed decode, B=32, 128 heads, S=16384",
