@@ -210,14 +210,14 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         if (t0 + BN <= fd.hi) {
 #pragma unroll
             for (int i = 0; i < STAGE_BLK; ++i)
-                dma16_off_at(((is_v_mask >> i) & 1) ? vg : kg, blk_off[i], stage + i * 1024);
+                dma16_off_at<true>(((is_v_mask >> i) & 1) ? vg : kg, blk_off[i], stage + i * 1024);
         } else {                                   // ragged tile: rows past the end re-read the last row
             const uint32_t lim = (uint32_t)(fd.hi - 1 - t0) * (D * 2);
 #pragma unroll
             for (int i = 0; i < STAGE_BLK; ++i) {
                 const uint32_t row_b = blk_off[i] & ~(uint32_t)(D * 2 - 1);
                 const uint32_t off = row_b > lim ? lim + (blk_off[i] & (D * 2 - 1)) : blk_off[i];
-                dma16_off_at(((is_v_mask >> i) & 1) ? vg : kg, off, stage + i * 1024);
+                dma16_off_at<true>(((is_v_mask >> i) & 1) ? vg : kg, off, stage + i * 1024);
             }
         }
         ++ft;

@@ -252,17 +252,31 @@ __device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base) {
 }
 
 // Same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
-// byte offset (the saddr form: one VGPR per address instead of two).
+// byte offset (the saddr form: one VGPR per address instead of two).  NT
+// marks data that is streamed once (decode caches): the copy carries the
+// non-temporal cache policy, so it does not displace reusable lines in L2 and
+// the memory-attached last-level cache.  Data that other workgroups re-read
+// (prefill K/V tiles) keeps the default policy.
+template <bool NT = false>
 __device__ __forceinline__ void dma16_off(const void *gbase, uint32_t off, const void *lds_base) {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_offset(lds_base));
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(off), "s"(gbase), "s"(m0v) : "memory");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                     :: "v"(off), "s"(gbase), "s"(m0v) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(off), "s"(gbase), "s"(m0v) : "memory");
 }
 // The same with the LDS destination given as a wave-uniform LDS byte address.
+template <bool NT = false>
 __device__ __forceinline__ void dma16_off_at(const void *gbase, uint32_t off, uint32_t lds_addr_u) {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr_u);
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(off), "s"(gbase), "s"(m0v) : "memory");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                     :: "v"(off), "s"(gbase), "s"(m0v) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(off), "s"(gbase), "s"(m0v) : "memory");
 }
 
 // 16-byte / 4-byte global stores issued through asm, for kernels that count

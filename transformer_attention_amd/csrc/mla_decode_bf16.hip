@@ -126,7 +126,7 @@ void mla_decode_kernel(Params p) {
 #pragma unroll
             for (int i = 0; i < 10; ++i) {
                 if (i >= my_nblk) break;
-                dma16_off(gbase, dma_off[i], stage + (my_blk0 + i) * 1024);
+                dma16_off<true>(gbase, dma_off[i], stage + (my_blk0 + i) * 1024);
             }
         } else {                                // ragged last tile: rows past the end re-read the last row
 #pragma unroll
@@ -134,7 +134,7 @@ void mla_decode_kernel(Params p) {
                 if (i >= my_nblk) break;
                 const uint32_t off = dma_row[i] > last
                     ? dma_off[i] - (uint32_t)((dma_row[i] - last) * ROWB) : dma_off[i];
-                dma16_off(gbase, off, stage + (my_blk0 + i) * 1024);
+                dma16_off<true>(gbase, off, stage + (my_blk0 + i) * 1024);
             }
         }
     };
