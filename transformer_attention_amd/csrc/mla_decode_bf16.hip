@@ -14,9 +14,10 @@
 //
 // gfx950 mapping:
 //  * 32-token tiles [32 x 576 bf16 = 36 KB] stream HBM -> LDS through a
-//    4-stage ring filled by global_load_lds_dwordx4 (no staging registers),
-//    three tiles in flight per CU while the fourth is consumed;
-//  * each tile is stored once, row-major with rows padded to 1168 bytes; the
+//    4-stage ring filled by global_load_lds_dwordx4 (no staging registers,
+//    non-temporal: the cache is read once), three tiles in flight per CU
+//    while the fourth is consumed;
+//  * each tile is stored once, row-major with rows 1216 bytes apart; the
 //    score product reads it with 16-byte loads, the P.V product reads the
 //    first 512 columns transposed with ds_read_b64_tr_b16, so the latent is
 //    never copied;
@@ -45,7 +46,7 @@ constexpr int LROW_SLOTS = 76;            // LDS row pitch in 16-byte slots (72 
 constexpr int LROW = LROW_SLOTS * 16;     // 1216 bytes
 constexpr int TILE_BYTES = 38 * 1024;     // 32 rows (last row ends at slot 2432) = 38 DMA blocks
 constexpr int NSTAGE = 4;
-constexpr int LDS_BYTES = NSTAGE * TILE_BYTES;   // 151552
+constexpr int LDS_BYTES = NSTAGE * TILE_BYTES;   // 155648
 constexpr int NW = 4;                     // waves per workgroup
 constexpr int HPW = 32;                   // heads per wave
 constexpr int HPC = NW * HPW;             // heads per workgroup (chunk)
@@ -99,10 +100,10 @@ void mla_decode_kernel(Params p) {
     const char *cg = reinterpret_cast<const char *>(p.c + (size_t)b * p.S_max * DK);
 
     // Issue the DMA of tile `t` (relative) into its ring stage: this wave's
-    // 1-KB blocks.  LDS byte o = 1024*blk + 16*lane of the stage holds
-    // (row o / 1168, chunk (o % 1168) / 16); the pad slot (chunk 72) and the
-    // bytes past row 31 receive an arbitrary valid chunk.  Rows past the
-    // chunk end re-read the last valid row (their scores are masked).
+    // 1-KB blocks.  LDS slot q = (1024*blk + 16*lane) / 16 of the stage holds
+    // row r = q / 76, chunk q - row_slot(r); the pad slots and the slots past
+    // row 31 receive an arbitrary valid chunk.  Rows past the chunk end
+    // re-read the last valid row (their scores are masked).
     const int my_blk0 = wave < 2 ? 10 * wave : 20 + 9 * (wave - 2);
     const int my_nblk = wave < 2 ? 10 : 9;
     // Byte offset (within a tile's 32 cache rows) that lane `lane` copies for
