@@ -190,6 +190,30 @@ def test_large_logits_stay_finite(ta, oracle_mod):
     assert_bf16_close(np32(o), ro, "large logits")
 
 
+@pytest.mark.parametrize("slope", [10.0, -10.0])
+def test_scores_rising_or_falling_along_the_keys(ta, oracle_mod, slope):
+    """Score of key j grows (or falls) by about 40 log2 units per 64-key tile,
+    so with a rising slope every tile's probabilities overflow the current
+    reference max and the running max moves on every tile; with a falling
+    slope every later tile underflows against the first one."""
+    g = torch.Generator().manual_seed(11)
+    B, T, hq, hkv = 1, 700, 4, 2
+    q = torch.randn(B, hq, T, 128, generator=g)
+    k = torch.randn(B, hkv, T, 128, generator=g)
+    v = torch.randn(B, hkv, T, 128, generator=g)
+    q[..., 0] = slope
+    k[..., 0] = 0.5 * torch.arange(T, dtype=torch.float32)
+    q, k, v = (x.to(torch.bfloat16).cuda() for x in (q, k, v))
+    scale = 1.0 / math.sqrt(128)
+    for window in (0, 200):
+        print(f"[case] slope {slope} window {window}", flush=True)
+        o, lse = _run(ta, q, k, v, True, window, scale)
+        ro, rl = _oracle(oracle_mod, q, k, v, True, window, scale)
+        assert torch.isfinite(o).all()
+        assert_bf16_close(np32(o), ro, f"slope {slope} window {window}")
+        assert_lse_close(np32(lse), rl, LSE_BF16_ABS, f"slope {slope} window {window}")
+
+
 def test_finite_values_at_masked_positions_do_not_leak(ta):
     """Huge finite K/V at future positions leave the output bit-identical."""
     g = torch.Generator().manual_seed(10)

@@ -37,13 +37,20 @@
 //    global_load_lds_dwordx4 (no staging registers): while a wave computes
 //    the scores of tile t+1 and the P.V product of tile t, tiles t+2 and t+3
 //    are in flight (one barrier per tile);
-//  * each wave is software-pipelined: the MFMAs of the scores of tile t+1
-//    are issued between the exp/sum/convert of the probabilities of tile t,
-//    and the row max of tile t+1 is taken after the P.V MFMAs of tile t, so
-//    the matrix cores and the vector ALUs of one wave work concurrently;
-//  * the reference max is only moved when a tile's row max exceeds it by
-//    more than 2^8 (exact: every exponent is taken against the same
-//    reference max that l and O carry), so the O rescale is rare;
+//  * each wave is software-pipelined: the score MFMAs of tile t+1 are
+//    issued around the probabilities of key block 1 of tile t, and the P.V
+//    MFMAs of tile t around the probabilities of key block 0 of tile t+1,
+//    so each product carries half of the exponentials and the matrix cores
+//    and the vector ALUs of one wave work concurrently;
+//  * no row max is taken in steady state: a tile's probabilities are taken
+//    against the row's current reference max and accepted when every
+//    lane's partial sum of them is at most 2^16 (no probability exceeds
+//    2^16, far from overflow).  Otherwise (rare) the tile's scores are
+//    recomputed from LDS, the reference max of the rows concerned moves to
+//    their true running max, and their l and O are rescaled.  Every
+//    exponent is taken against the reference that l and O carry, so the
+//    quotient O / l is the same.  A row's first reference max is the row
+//    max of its first tile with a visible key;
 //  * workgroups are ordered heaviest row-block first (causal), and the
 //    head-group index is the fastest-varying part of the workgroup id, so
 //    with 8 (or a multiple of 8) head groups every workgroup of one K/V head
@@ -60,7 +67,10 @@ constexpr int ROWB = D * 2 + 48;   // LDS row stride of a K row (304 B = 19 slot
 constexpr int VROWB = D * 2 + 64;  // LDS row stride of a V row (320 B = 20 slots)
 constexpr int LDS_BUDGET = 160 * 1024;
 constexpr int WG_ROWS = 256;    // query rows x heads per workgroup
-constexpr float TAU = 8.0f;     // lazy-rescale threshold, log2 units
+// A tile is accepted against the current reference max when every lane's
+// partial row sum of its probabilities stays at or below THR (so no single
+// probability exceeds 2^16); otherwise the tile's true row max is taken.
+constexpr float THR = 65536.0f;
 
 #ifndef PREFILL_NB
 #define PREFILL_NB 1
@@ -165,12 +175,11 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[nb][db][i] = 0.f;
-    float m_run[NB], l_run[NB], mx_cur[NB];
+    float m_run[NB], l_run[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         m_run[nb] = -INFINITY;                        // reference max (log2 units)
         l_run[nb] = 0.f;                              // lane-partial row sum
-        mx_cur[nb] = -INFINITY;                       // scaled max of the pending tile
     }
 
     // LDS ring of NSTAGE stages, each holding the K and V rows of one tile.
@@ -304,17 +313,55 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
         const bf16x4 hi4 = lds_read_tr16(vt + vtile_off(rA + 8, ch) + v_byte_lane);
         return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    // Probabilities of key block kb (16 values) -> two bf16x8 B operands; adds to lsum.
-    // The row sum adds the bf16-rounded probabilities (two per v_dot2 with
-    // (1, 1)): the same weights the P.V product uses.
-    auto probs = [&](const f32x16 &s, float m_use, float &lsum, bf16x8 &p0, bf16x8 &p1) {
-        float pv[16];
+    // Probabilities of scores 8h .. 8h+7 of a key block against the reference
+    // max m_use -> one bf16x8 B operand (keys 8(h/2)+4hi.. of the two row
+    // groups of that half); adds them to lsum.  The row sum adds the
+    // bf16-rounded probabilities (two per v_dot2 with (1, 1)): the same
+    // weights the P.V product uses.
+    auto probs8 = [&](const f32x16 &s, int h, float m_use, float &lsum, bf16x8 &pp) {
+        float pv[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(s[i], c, -m_use));
-        p0 = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-        p1 = to_bf16x8(pv[8], pv[9], pv[10], pv[11], pv[12], pv[13], pv[14], pv[15]);
-        lsum = sum_bf16x8(p0, lsum);
-        lsum = sum_bf16x8(p1, lsum);
+        for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(__builtin_fmaf(s[8 * h + i], c, -m_use));
+        pp = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        lsum = sum_bf16x8(pp, lsum);
+    };
+    // Exponents are taken against 0 while a row has seen no visible key.
+    auto m_ref = [](float m) { return m == -INFINITY ? 0.f : m; };
+    // Keep a value computed where it is written: the IR optimisers would
+    // otherwise sink the probabilities of one product into the next.
+    auto pin = [](bf16x8 &x) { asm volatile("" : "+v"(x)); };
+
+    // The probabilities of key block 0 of the next tile (and their lane-partial
+    // sum) are computed one product ahead: during the P.V MFMAs of the
+    // current tile.  Key block 1 follows during the next score MFMAs.
+    static_assert(KB == 2, "the probability schedule splits a tile into two 32-key blocks");
+    bf16x8 pc[NB][2];
+    float lc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) lc[nb] = 0.f;
+    // A row's reference max is first set to the row max of the first tile in
+    // which it has a visible key, before any of that tile's probabilities
+    // are taken.  rows_started turns true (wave-uniform) once every row of
+    // the wave below T has one, and the row max is not taken after that.
+    bool rows_started = false;
+    auto start_rows = [&](const f32x16 (&s)[NB][KB]) {
+        bool done = true;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float mx = tile_max(s[nb]);
+            if (m_run[nb] == -INFINITY) m_run[nb] = mx;
+            done = done && (m_run[nb] != -INFINITY || row0 + 32 * nb >= T);
+        }
+        rows_started = __all(done);
+    };
+    // Probabilities of key block 0 of a tile, one product ahead.
+    auto probs_block0 = [&](const f32x16 (&s)[NB][KB]) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            lc[nb] = 0.f;
+            probs8(s[nb][0], 0, m_ref(m_run[nb]), lc[nb], pc[nb][0]);
+            probs8(s[nb][0], 1, m_ref(m_run[nb]), lc[nb], pc[nb][1]);
+        }
     };
 
     // ---- prologue: tiles tb .. tb+AHEAD-1 in flight; S(tb) and its max ----
@@ -328,9 +375,42 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
     if (tile_active(t_begin)) {
         qk(kbuf(0), sa);
         if (tile_needs_mask(t_begin)) apply_mask(t_begin, sa);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = tile_max(sa[nb]);
+        start_rows(sa);
+        probs_block0(sa);
     }
+
+    // Some row of tile t overflowed the threshold: recompute the tile's scores from the K rows still in its stage
+    // (bit for bit the same scores), move those rows' reference max to their
+    // true running max, rescale their l and O, and recompute the tile's
+    // probabilities.  Rows that did not ask keep their reference max, so
+    // their probabilities come out unchanged and every row's result depends
+    // on its own scores only.
+    auto rescale_tile = [&](int t, const bool (&redo)[NB], float (&m_use)[NB], float (&lsum)[NB],
+                            bf16x8 (&pop)[NB][KB][2]) {
+        f32x16 sr[NB][KB];
+        qk(kbuf(t - t_begin), sr);
+        if (tile_needs_mask(t)) apply_mask(t, sr);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const bool row_redo = pair32_max(redo[nb] ? 1.0f : 0.0f) > 0.f;   // either lane of the row
+            const float m_new = row_redo ? fmaxf(m_run[nb], tile_max(sr[nb])) : m_run[nb];
+            const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run[nb] - m_new);
+            l_run[nb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                if constexpr (ASM_S) scale_acc(oacc[nb][db], alpha);
+                else oacc[nb][db] *= alpha;
+            }
+            m_run[nb] = m_new;
+            m_use[nb] = m_ref(m_new);
+            lsum[nb] = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                probs8(sr[nb][kb], 0, m_use[nb], lsum[nb], pop[nb][kb][0]);
+                probs8(sr[nb][kb], 1, m_use[nb], lsum[nb], pop[nb][kb][1]);
+            }
+        }
+    };
 
     // One iteration: softmax + P.V of tile t (scores in s_cur), scores of
     // tile t+1 into s_nxt.
@@ -347,39 +427,21 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
         const char *kn = kbuf(rel + 1);
         const char *vc = vbuf(rel);
 
-        float m_use[NB];
         if (act_c) {
-            bool any_upd = false;
-            float alpha[NB];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const bool upd = mx_cur[nb] > m_run[nb] + TAU;
-                const float m_new = upd ? mx_cur[nb] : m_run[nb];
-                alpha[nb] = upd ? fast_exp2(m_run[nb] - m_new) : 1.0f;
-                any_upd = any_upd || __any(upd);
-                l_run[nb] *= alpha[nb];
-                m_run[nb] = m_new;
-                m_use[nb] = (m_new == -INFINITY) ? 0.f : m_new;
-            }
-            if (any_upd) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) {
-                        if constexpr (ASM_S) scale_acc(oacc[nb][db], alpha[nb]);
-                        else oacc[nb][db] *= alpha[nb];
-                    }
-            }
-        }
-
-        if (act_c) {
-            // scores of tile t+1 interleaved with the probabilities of tile t
-            // (when t+1 is not this wave's, the scores are computed and dropped:
-            // the stage holds valid LDS data and s_nxt is not used)
-            float lsum[NB];
+            // Key block 0 of tile t was done one product ahead; block 1 runs
+            // between the score MFMAs of tile t+1 (when t+1 is not this
+            // wave's, its scores are computed from whatever its stage holds
+            // and dropped: s_nxt and the probabilities made from it are not
+            // used).
+            float m_use[NB], lsum[NB];
             bf16x8 pop[NB][KB][2];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) lsum[nb] = 0.f;
+            for (int nb = 0; nb < NB; ++nb) {
+                m_use[nb] = m_ref(m_run[nb]);
+                lsum[nb] = lc[nb];
+                pop[nb][0][0] = pc[nb][0];
+                pop[nb][0][1] = pc[nb][1];
+            }
             // K operands are loaded KPF k-steps ahead of their MFMAs
             constexpr int KPF = 2;
             bf16x8 ka[KPF + 1][KB];
@@ -401,22 +463,31 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) smfma(ks, kb, nb, ka[ks % (KPF + 1)][kb], s_nxt[nb][kb]);
                 if (ks == 1 && dma_now) issue_tile(t + AHEAD);
-                // spread the NB*KB probability blocks over the 8 MFMA steps
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-                        if (ks == 1 + (6 * (nb * KB + kb)) / (NB * KB))
-                            probs(s_cur[nb][kb], m_use[nb], lsum[nb], pop[nb][kb][0], pop[nb][kb][1]);
+                for (int nb = 0; nb < NB; ++nb) {
+                    if (ks == 1) { probs8(s_cur[nb][1], 0, m_use[nb], lsum[nb], pop[nb][1][0]); pin(pop[nb][1][0]); }
+                    if (ks == 4) { probs8(s_cur[nb][1], 1, m_use[nb], lsum[nb], pop[nb][1][1]); pin(pop[nb][1][1]); }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // Accept tile t unless a lane's partial sum passed the threshold
+            // (or is not a number).
+            bool redo[NB], any_redo = false;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                redo[nb] = !(lsum[nb] <= THR);
+                any_redo = any_redo || redo[nb];
+            }
+            if (__any(any_redo)) rescale_tile(t, redo, m_use, lsum, pop);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) l_run[nb] += lsum[nb];
-            // row max of tile t+1, spread over the P.V MFMAs below
             if (act_n && tile_needs_mask(t + 1)) apply_mask(t + 1, s_nxt);
-            float mpart[NB];
+            if (!rows_started && act_n) {
+                start_rows(s_nxt);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) mpart[nb] = -INFINITY;
+                for (int nb = 0; nb < NB; ++nb) m_use[nb] = m_ref(m_run[nb]);
+            }
+            // P.V of tile t; key block 0 of tile t+1 is exponentiated under it
             // V operands are loaded VPF MFMA steps ahead
             constexpr int NV = KB * 2 * 4;            // (kb, half, db) steps
             constexpr int VPF = 3;
@@ -433,29 +504,20 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
                     if constexpr (ASM_S) mfma_o_acc(va[j % (VPF + 1)], pop[nb][kb][half], oacc[nb][db]);
                     else oacc[nb][db] = mfma32x32x16(va[j % (VPF + 1)], pop[nb][kb][half], oacc[nb][db]);
                 }
-                // 8 scores of s_nxt per step for the first NB*KB*2 steps
-                if (j < 2 * NB * KB) {
-                    const int nb = j / (2 * KB), kb = (j / 2) % KB, h8 = 8 * (j & 1);
-                    float m8 = fmaxf(fmaxf(fmaxf(s_nxt[nb][kb][h8], s_nxt[nb][kb][h8 + 1]),
-                                           fmaxf(s_nxt[nb][kb][h8 + 2], s_nxt[nb][kb][h8 + 3])),
-                                     fmaxf(fmaxf(s_nxt[nb][kb][h8 + 4], s_nxt[nb][kb][h8 + 5]),
-                                           fmaxf(s_nxt[nb][kb][h8 + 6], s_nxt[nb][kb][h8 + 7])));
-                    mpart[nb] = fmaxf(mpart[nb], m8);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    if (j == 2) { lc[nb] = 0.f; probs8(s_nxt[nb][0], 0, m_use[nb], lc[nb], pc[nb][0]); pin(pc[nb][0]); }
+                    if (j == 8) { probs8(s_nxt[nb][0], 1, m_use[nb], lc[nb], pc[nb][1]); pin(pc[nb][1]); }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = act_n ? pair32_max(mpart[nb]) * c : -INFINITY;
         } else {
             if (dma_now) issue_tile(t + AHEAD);
-            if (act_n) {
+            if (act_n) {                              // first tile of this wave
                 qk(kn, s_nxt);
                 if (tile_needs_mask(t + 1)) apply_mask(t + 1, s_nxt);
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = tile_max(s_nxt[nb]);
-            } else {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) mx_cur[nb] = -INFINITY;
+                start_rows(s_nxt);
+                probs_block0(s_nxt);
             }
         }
     };
