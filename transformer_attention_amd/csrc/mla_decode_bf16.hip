@@ -166,6 +166,7 @@ void mla_decode_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
+    float thr_raw = -INFINITY;              // raw-score level that moves the reference max
 
     // C^T operand (32 d x 16 tokens) through the transposing read.  K slot j
     // of lane half hh in token step kk is token 16kk + 8(j/4) + 4hh + (j%4),
@@ -227,16 +228,23 @@ void mla_decode_kernel(Params p) {
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-        mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
-        const bool upd = mx > m_run + TAU;
-        const float m_new = upd ? mx : m_run;
-        const float alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
-        m_run = m_new;
-        if (t > 0 && __any(upd)) {              // before tile 0 the output is still zero
+        // The reference max moves only when some lane's raw score exceeds
+        // thr_raw = (m_run + TAU) / scale_log2 (tile 0 always: thr_raw starts
+        // at -inf).  Only then is the head's max taken over both lane halves.
+        float alpha = 1.0f;
+        if (__any(mx > thr_raw)) {
+            const float mxp = pair32_max(mx) * p.scale_log2;
+            const bool upd = mxp > m_run + TAU;
+            const float m_new = upd ? mxp : m_run;
+            alpha = upd ? fast_exp2(m_run - m_new) : 1.0f;
+            if (t > 0) {                        // before tile 0 the output is still zero
 #pragma unroll
-            for (int db = 0; db < DC / 32; ++db) scale_acc(oacc[db], alpha);
+                for (int db = 0; db < DC / 32; ++db) scale_acc(oacc[db], alpha);
+            }
+            m_run = m_new;
+            thr_raw = (m_run + TAU) / p.scale_log2;
         }
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         // p = 2^(s * scale_log2 - m): one FMA and one exp per score
         // (computed in place: sacc[i] becomes the probability of score i)
 #pragma unroll
@@ -282,7 +290,7 @@ void mla_decode_kernel(Params p) {
         l_run = l_run * alpha + lsum;
     }
 
-    const float lt = l_run + shfl_xor(l_run, 32);
+    const float lt = pair32_sum(l_run);
     if (!head_ok) return;
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const size_t ws = ((size_t)b * p.H + h) * p.n_split_max + s;
