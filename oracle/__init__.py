@@ -14,7 +14,10 @@ float64.
 Pages the definitions follow (cited by title and section):
   * "Attention Engineering: From MHA to GQA, MLA & FlashAttention", section 2
     (GQA formulation), section 3 (MLA absorbed score and output), section 4
-    (online-softmax state and log-sum-exp), section 5 (KV-cache byte formula).
+    (online-softmax state and log-sum-exp, kept for the backward pass),
+    section 5 (KV-cache byte formula).
+  * "Attention, Worked Out by Hand (Part 2)", section 2 (the backward pass
+    recomputes the scores).
   * "Attention deep dive (MHA -> MQA -> GQA -> FlashAttention)", section 5
     (decode against the cache) and section 6 (sliding-window mask).
   * "2.4 Multi-Head Attention, MQA, GQA & MLA", "Implementing the MHA -> GQA
@@ -62,6 +65,8 @@ def _load():
     D = ctypes.c_double
     lib.oracle_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, D, P, I]
     lib.oracle_prefill.restype = I
+    lib.oracle_prefill_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, D]
+    lib.oracle_prefill_backward.restype = I
     lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D]
     lib.oracle_decode.restype = I
     lib.oracle_mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, D]
@@ -122,6 +127,26 @@ def prefill(q, k, v, *, causal: bool, window: int = 0, scale: float,
     if rc != 0:
         raise ValueError("oracle_prefill: invalid shape")
     return o, lse
+
+
+def prefill_backward(q, k, v, dout, *, causal: bool, window: int = 0, scale: float):
+    """Gradients of the exact attention forward with respect to q, k, v for
+    the output gradient ``dout``.  q, dout:[B,hq,T,d]  k,v:[B,hkv,T,d].
+    Returns (dq, dk, dv) float64, shaped like q, k, v; dk and dv sum over the
+    query heads of each K/V group."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, hq, T, d = q.shape
+    hkv = k.shape[1]
+    assert k.shape == (B, hkv, T, d) and v.shape == k.shape and dout.shape == q.shape
+    dq = np.zeros((B, hq, T, d), dtype=np.float64)
+    dk = np.zeros((B, hkv, T, d), dtype=np.float64)
+    dv = np.zeros((B, hkv, T, d), dtype=np.float64)
+    rc = _load().oracle_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                         _ptr(dq), _ptr(dk), _ptr(dv), B, T, hq, hkv, d,
+                                         int(bool(causal)), int(window), float(scale))
+    if rc != 0:
+        raise ValueError("oracle_prefill_backward: invalid shape")
+    return dq, dk, dv
 
 
 def decode(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale: float):

@@ -135,6 +135,127 @@ int oracle_prefill(const float *q, const float *k, const float *v,
 }
 
 /*
+ * Prefill backward: the gradients of the prefill forward above with respect
+ * to q, k and v, given the gradient dO of its output.
+ *
+ * The pages keep only the per-row log-sum-exp of the forward for the
+ * backward pass and have it recompute the scores ("Attention Engineering
+ * ...", section 4, the text after the FlashAttention-2 recurrence;
+ * "Attention, Worked Out by Hand (Part 2)", section 2).  The gradient itself
+ * is the chain rule applied to the plain forward, with every score row
+ * materialised (P_ij the softmax weight of visible key j in row i, 0 for a
+ * masked key):
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ * where for K and V the sums over i also run over the query heads of the
+ * group that shares them.
+ *
+ * Two plain passes: the first goes over query rows (log-sum-exp, the row
+ * dot product sum_j P_ij dP_ij, and dQ_i); the second over keys of each
+ * K/V head (dK_j, dV_j), recomputing P_ij = exp(s_ij - lse_i).
+ * q, dout:[B,hq,T,d]  k,v:[B,hkv,T,d]  (float);  dq:[B,hq,T,d],
+ * dk,dv:[B,hkv,T,d] (double).  Returns 0, or -1 for an invalid shape.
+ */
+int oracle_prefill_backward(const float *q, const float *k, const float *v,
+                            const float *dout, double *dq, double *dk, double *dv,
+                            int B, int T, int hq, int hkv, int d,
+                            int causal, int window, double scale)
+{
+    if (B < 0 || T < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv) return -1;
+    const int G = hq / hkv;
+    const long rows = (long)B * hq * T;
+    double *lse = (double *)malloc(sizeof(double) * (rows > 0 ? rows : 1));
+    double *rdot = (double *)malloc(sizeof(double) * (rows > 0 ? rows : 1));
+    if (!lse || !rdot) { free(lse); free(rdot); return -1; }
+    /* pass 1: one query row at a time */
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (T > 0 ? T : 1));
+        double *dp = (double *)malloc(sizeof(double) * (T > 0 ? T : 1));
+        unsigned char *vis = (unsigned char *)malloc(T > 0 ? T : 1);
+#pragma omp for schedule(dynamic, 16)
+        for (long u = 0; u < rows; ++u) {
+            const long i = u % T;
+            const long h = (u / T) % hq;
+            const long b = u / ((long)T * hq);
+            const long g = h / G;
+            const float *qi = q + u * d;
+            const float *doi = dout + u * d;
+            const float *kb = k + ((b * hkv + g) * (long)T) * d;
+            const float *vb = v + ((b * hkv + g) * (long)T) * d;
+            double m = -INFINITY;
+            int any = 0;
+            for (long j = 0; j < T; ++j) {
+                vis[j] = (unsigned char)prefill_visible(i, j, causal, window);
+                double acc = 0.0, accv = 0.0;
+                for (int t = 0; t < d; ++t) {
+                    acc += (double)qi[t] * (double)kb[j * d + t];
+                    accv += (double)doi[t] * (double)vb[j * d + t];
+                }
+                s[j] = acc * scale;
+                dp[j] = accv;
+                if (vis[j]) { if (!any || s[j] > m) m = s[j]; any = 1; }
+            }
+            double *dqi = dq + u * d;
+            for (int t = 0; t < d; ++t) dqi[t] = 0.0;
+            if (!any) { lse[u] = -INFINITY; rdot[u] = 0.0; continue; }
+            double l = 0.0;
+            for (long j = 0; j < T; ++j)
+                if (vis[j]) l += exp(s[j] - m);
+            const double L = m + log(l);
+            double rd = 0.0;
+            for (long j = 0; j < T; ++j)
+                if (vis[j]) rd += exp(s[j] - L) * dp[j];
+            lse[u] = L;
+            rdot[u] = rd;
+            for (long j = 0; j < T; ++j) {
+                if (!vis[j]) continue;
+                const double ds = exp(s[j] - L) * (dp[j] - rd);
+                for (int t = 0; t < d; ++t) dqi[t] += scale * ds * (double)kb[j * d + t];
+            }
+        }
+        free(s); free(dp); free(vis);
+    }
+    /* pass 2: one key of one K/V head at a time, over the group's query rows */
+    const long keys = (long)B * hkv * T;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long u = 0; u < keys; ++u) {
+        const long j = u % T;
+        const long g = (u / T) % hkv;
+        const long b = u / ((long)T * hkv);
+        const float *kj = k + u * d;
+        const float *vj = v + u * d;
+        double *dkj = dk + u * d;
+        double *dvj = dv + u * d;
+        for (int t = 0; t < d; ++t) { dkj[t] = 0.0; dvj[t] = 0.0; }
+        for (long h = g * G; h < (g + 1) * G; ++h) {
+            for (long i = 0; i < T; ++i) {
+                if (!prefill_visible(i, j, causal, window)) continue;
+                const long r = ((b * hq + h) * (long)T) + i;
+                const float *qi = q + r * d;
+                const float *doi = dout + r * d;
+                double acc = 0.0, accv = 0.0;
+                for (int t = 0; t < d; ++t) {
+                    acc += (double)qi[t] * (double)kj[t];
+                    accv += (double)doi[t] * (double)vj[t];
+                }
+                const double p = exp(acc * scale - lse[r]);
+                const double ds = p * (accv - rdot[r]);
+                for (int t = 0; t < d; ++t) {
+                    dvj[t] += p * (double)doi[t];
+                    dkj[t] += scale * ds * (double)qi[t];
+                }
+            }
+        }
+    }
+    free(lse); free(rdot);
+    return 0;
+}
+
+/*
  * Single-token decode against a KV cache.
  * q:[B,hq,d]  kc,vc:[B,hkv,S_max,d]  seq_lens[B] (valid cached length of
  * sequence b, already including the current token).  The query is the
