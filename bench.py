@@ -9,8 +9,10 @@ also measures the two decode forms on their workloads -- 70B-shaped GQA
 decode (B=64, 64/8 heads, cached lengths uniform in [4096, 32768]) and
 DeepSeek-V3-shaped MLA absorbed decode (B=32, 128 heads, 16384 tokens of
 576 values) -- in KV-cache GB/s, counting only cache rows inside each
-sequence plus q and o -- and the two sliding-window prefills (B=4, T=4096,
-32 query heads, window 1024, with 32 and with 1 K/V head) in TFLOP/s.
+sequence plus q and o -- the two sliding-window prefills (B=4, T=4096,
+32 query heads, window 1024, with 32 and with 1 K/V head) in TFLOP/s, and
+the backward (dQ, dK, dV) of the Llama-3-8B prefill in TFLOP/s, counting
+10*d_h FLOP per visible pair (five products).
 
 Inputs are seeded synthetic N(0,1) tensors (workloads.py), resident in HBM
 before timing.  W untimed warm-up steps, then exactly K timed steps between
@@ -18,7 +20,7 @@ two device synchronisations; kernel durations come from HIP events recorded
 on the stream the kernels run on.  One JSON line is printed.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|decode|mla|swa-mha|swa-mqa|copy]
+                    [--only prefill|backward|decode|mla|swa-mha|swa-mqa|copy]
 
 ``--only copy`` times a plain 1 GiB device copy instead: it is the
 calibration run for rocprofv3's HBM byte counters, not an attention bench.
@@ -80,6 +82,34 @@ def bench_prefill(torch, ta, W, shape, steps, warmup):
     flops = prefill_flops(shape)
     tflops = flops / (ms * 1e-3) / 1e12
     del q, k, v, o
+    return {"ms": ms, "wall_s": wall, "flops": flops, "tflops": tflops,
+            "frac_bf16_peak": tflops / BF16_PEAK_TFLOPS}
+
+
+def backward_flops(shape) -> int:
+    """Five products per visible pair and head (S recomputed, dP, dV, dK, dQ), 2 d_h each;
+    the scores and dP that the dQ pass recomputes are not credited."""
+    return 10 * shape.B * shape.h_q * shape.d_h * prefill_visible_pairs(shape.T, shape.causal,
+                                                                         shape.window)
+
+
+def bench_backward(torch, ta, W, shape, steps, warmup):
+    q, k, v = W.prefill_inputs(shape, seed=0, device="cuda", gen_device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(1)
+    do = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    o, lse = ta.attn_prefill(q, k, v, causal=shape.causal, window=shape.window, scale=shape.scale,
+                             return_lse=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ta.attn_prefill_backward_workspace_size(shape.B, shape.T, shape.h_q),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = lambda: ta.attn_prefill_backward(q, k, v, o, do, lse, causal=shape.causal,
+                                          window=shape.window, scale=shape.scale, dq=dq, dk=dk,
+                                          dv=dv, workspace=ws)
+    ms, wall = _events_time(torch, fn, steps, warmup, stream)
+    flops = backward_flops(shape)
+    tflops = flops / (ms * 1e-3) / 1e12
+    del q, k, v, do, o, lse, dq, dk, dv, ws
     return {"ms": ms, "wall_s": wall, "flops": flops, "tflops": tflops,
             "frac_bf16_peak": tflops / BF16_PEAK_TFLOPS}
 
@@ -182,7 +212,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    choices=["prefill", "decode", "mla", "swa-mha", "swa-mqa", "copy"])
+                    choices=["prefill", "backward", "decode", "mla", "swa-mha", "swa-mqa",
+                             "copy"])
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -210,6 +241,10 @@ def main(argv=None):
         out["swa_mha"] = bench_prefill(torch, ta, W, W.SWA_MHA, args.steps, args.warmup)
     if only in (None, "swa-mqa"):
         out["swa_mqa"] = bench_prefill(torch, ta, W, W.SWA_MQA, args.steps, args.warmup)
+    if only in (None, "backward"):
+        out["backward"] = bench_backward(torch, ta, W, shape, args.steps, args.warmup)
+        print(f"[bench] backward {out['backward']['ms']:.3f} ms "
+              f"{out['backward']['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     if only == "copy":
         out["copy"] = bench_copy(torch, args.steps, args.warmup)
     if only in (None, "decode"):
@@ -266,6 +301,11 @@ def main(argv=None):
             r = out[key]
             line[key] = {"workload": name, "ms": round(r["ms"], 4), "TFLOP_s": round(r["tflops"], 2),
                          "frac_bf16_peak": round(r["frac_bf16_peak"], 4), "flops": r["flops"]}
+    if "backward" in out and next(iter(out)) != "backward":
+        r = out["backward"]
+        line["backward"] = {"workload": "Llama-3-8B-shaped causal GQA prefill backward (dQ, dK, dV)",
+                            "ms": round(r["ms"], 4), "TFLOP_s": round(r["tflops"], 2),
+                            "frac_bf16_peak": round(r["frac_bf16_peak"], 4), "flops": r["flops"]}
     if "mla" in out:
         m = out["mla"]
         line["mla"] = {"workload": "DeepSeek-V3-shaped MLA absorbed decode, B=32, 128 heads, S=16384",

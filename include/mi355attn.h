@@ -86,6 +86,43 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
                            hipStream_t stream);
 
 /*
+ * attn_prefill_backward -- gradients of attn_prefill with respect to q, k, v.
+ *
+ *   q, o, dout : [B, h_q,  T, d_h]  dtype    (read; o and lse are what
+ *   lse        : [B, h_q,  T]       float32   attn_prefill returned for q, k, v)
+ *   k, v       : [B, h_kv, T, d_h]  dtype    (read)
+ *   dq         : [B, h_q,  T, d_h]  dtype    (written)
+ *   dk, dv     : [B, h_kv, T, d_h]  dtype    (written; each K/V head's
+ *                gradient sums over the h_q / h_kv query heads that share it)
+ *
+ * The forward keeps only the per-row log-sum-exp for this pass, and the
+ * scores are recomputed from q and k ("Attention Engineering ...", section
+ * 4, the text after the FlashAttention-2 recurrence; "Attention, Worked Out
+ * by Hand (Part 2)", section 2): on visible keys P_ij = exp(scale q_i.k_j -
+ * lse_i).  With dP_ij = dout_i.v_j and D_i = dout_i.o_i:
+ *   dS_ij = P_ij (dP_ij - D_i),   dq_i = scale sum_j dS_ij k_j,
+ *   dk_j = scale sum_i dS_ij q_i, dv_j = sum_i P_ij dout_i,
+ * the derivative of the forward.  causal, window and scale must be the ones
+ * the forward used.  Accumulation is fp32; P and dS are rounded to bf16 as
+ * MFMA operands and the outputs to bf16 (round-to-nearest-even).  No atomics:
+ * the result is bitwise reproducible.
+ *
+ * workspace: caller device memory of at least
+ * attn_prefill_backward_workspace_size(B, T, h_q) bytes (per-row lse in log2
+ * units and D, rows padded to a multiple of 64); it is overwritten.
+ * Supported: dtype ATTN_BF16 with d_h = 128 (ATTN_ERR_UNSUPPORTED otherwise).
+ * Returns 0 from the size function for invalid sizes.
+ */
+size_t attn_prefill_backward_workspace_size(int B, int T, int h_q);
+attn_status_t attn_prefill_backward(const void *q, const void *k, const void *v,
+                                    const void *o, const void *dout, const float *lse,
+                                    void *dq, void *dk, void *dv,
+                                    int B, int T, int h_q, int h_kv, int d_h,
+                                    attn_dtype_t dtype, int causal, int window, float scale,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
  * attn_decode -- one new query token per sequence against a bf16 KV cache
  * ("Attention deep dive ...", section 5 "The KV cache": the new query
  * attends to every cached key, cached + new, so no causal mask applies

@@ -190,6 +190,9 @@ int oracle_prefill_backward(const float *q, const float *k, const float *v,
             int any = 0;
             for (long j = 0; j < T; ++j) {
                 vis[j] = (unsigned char)prefill_visible(i, j, causal, window);
+                s[j] = 0.0;
+                dp[j] = 0.0;
+                if (!vis[j]) continue;
                 double acc = 0.0, accv = 0.0;
                 for (int t = 0; t < d; ++t) {
                     acc += (double)qi[t] * (double)kb[j * d + t];
@@ -197,7 +200,8 @@ int oracle_prefill_backward(const float *q, const float *k, const float *v,
                 }
                 s[j] = acc * scale;
                 dp[j] = accv;
-                if (vis[j]) { if (!any || s[j] > m) m = s[j]; any = 1; }
+                if (!any || s[j] > m) m = s[j];
+                any = 1;
             }
             double *dqi = dq + u * d;
             for (int t = 0; t < d; ++t) dqi[t] = 0.0;

@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("attn_prefill", "attn_decode", "mla_decode", "attn_decode_workspace_size",
+    for n in ("attn_prefill", "attn_prefill_backward", "attn_prefill_backward_workspace_size",
+              "attn_decode", "mla_decode", "attn_decode_workspace_size",
               "mla_decode_workspace_size", "attn_status_string", "attn_abi_version"):
         assert n in names, n
 
@@ -74,6 +75,31 @@ def test_prefill_validation(lib):
     assert _prefill(lib, d=64) == 2                 # bf16 kernel is d = 128
     assert _prefill(lib, dtype=0, d=48) == 2        # fp32 d not instantiated
     assert _prefill(lib, dtype=7) == 2
+
+
+def test_prefill_backward_validation(lib):
+    def bwd(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+                 B=1, T=100, hq=4, hkv=2, d=128, dtype=1, causal=1, window=0, scale=0.1,
+                 ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.attn_prefill_backward(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
+                                         a["dq"], a["dk"], a["dv"], a["B"], a["T"], a["hq"],
+                                         a["hkv"], a["d"], a["dtype"], a["causal"], a["window"],
+                                         a["scale"], a["ws"], a["wsb"], None)
+    assert bwd(lse=None) == 1
+    assert bwd(dk=None) == 1
+    assert bwd(T=0) == 1
+    assert bwd(hq=6, hkv=4) == 1
+    assert bwd(window=5, causal=0) == 1
+    assert bwd(scale=0.0) == 1
+    assert bwd(d=64) == 2
+    assert bwd(dtype=0) == 2                        # backward is bf16 only
+    assert bwd(ws=None) == 3
+    need = lib.attn_prefill_backward_workspace_size(1, 100, 4)
+    assert need >= 1 * 4 * 128 * 8                  # rows padded to 128, two floats each
+    assert bwd(wsb=need - 1) == 3
+    assert lib.attn_prefill_backward_workspace_size(0, 100, 4) == 0
 
 
 def test_decode_validation(lib):

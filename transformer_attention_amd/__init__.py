@@ -9,6 +9,8 @@ library is not built, importing the entry points raises.
 
 Entry points (same names as the C ABI):
   attn_prefill(q, k, v, *, causal, window=0, scale=None, o=None, lse=None)
+  attn_prefill_backward(q, k, v, o, dout, lse, *, causal, window=0, scale=None,
+                        dq=None, dk=None, dv=None, workspace=None)
   attn_decode(q, k_cache, v_cache, seq_lens, *, window=0, scale=None,
               split_tokens=0, o=None, lse=None, workspace=None)
   mla_decode(q, kv_cache, seq_lens, *, d_c=512, d_r=64, scale,
@@ -36,7 +38,8 @@ ATTN_F32 = 0
 ATTN_BF16 = 1
 
 EXPORTED_SYMBOLS = (
-    "attn_prefill", "attn_decode", "attn_decode_workspace_size",
+    "attn_prefill", "attn_prefill_backward", "attn_prefill_backward_workspace_size",
+    "attn_decode", "attn_decode_workspace_size",
     "mla_decode", "mla_decode_workspace_size", "attn_status_string",
     "attn_abi_version",
 )
@@ -63,6 +66,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
     lib.attn_prefill.restype = I
+    lib.attn_prefill_backward_workspace_size.argtypes = [I, I, I]
+    lib.attn_prefill_backward_workspace_size.restype = Z
+    lib.attn_prefill_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F,
+                                          P, Z, P]
+    lib.attn_prefill_backward.restype = I
     lib.attn_decode_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.attn_decode_workspace_size.restype = Z
     lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
@@ -146,6 +154,49 @@ def attn_prefill(q, k, v, *, causal: bool = True, window: int = 0, scale=None,
                           float(scale), _stream(q.device))
     _check(st, "attn_prefill")
     return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_prefill_backward_workspace_size(B, T, h_q) -> int:
+    return int(load_library().attn_prefill_backward_workspace_size(B, T, h_q))
+
+
+def attn_prefill_backward(q, k, v, o, dout, lse, *, causal: bool = True, window: int = 0,
+                          scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of attn_prefill.  q, o, dout:[B,h_q,T,128] bf16; k,v:[B,h_kv,T,128]
+    bf16; lse:[B,h_q,T] fp32 (the forward's).  Returns (dq, dk, dv)."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16, ndim=4)
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _require(t, name, torch.bfloat16, q.device, 4)
+    _require(lse, "lse", torch.float32, q.device)
+    B, hq, T, d = q.shape
+    hkv = k.shape[1]
+    if tuple(k.shape) != (B, hkv, T, d) or tuple(v.shape) != (B, hkv, T, d):
+        raise ValueError("k/v shape mismatch")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o/dout shape mismatch")
+    if lse.numel() != B * hq * T:
+        raise ValueError("lse shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _require(dq, "dq", torch.bfloat16, q.device)
+    _require(dk, "dk", torch.bfloat16, q.device)
+    _require(dv, "dv", torch.bfloat16, q.device)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("gradient shape mismatch")
+    need = attn_prefill_backward_workspace_size(B, T, hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", torch.uint8, q.device)
+    st = lib.attn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, T, hq, hkv, d,
+                                   _DT[q.dtype], int(bool(causal)), int(window), float(scale),
+                                   _ptr(workspace), workspace.numel(), _stream(q.device))
+    _check(st, "attn_prefill_backward")
+    return dq, dk, dv
 
 
 def attn_decode_workspace_size(B, S_max, h_q, h_kv, d_h, split_tokens=0) -> int:

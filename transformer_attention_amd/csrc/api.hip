@@ -98,6 +98,35 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+size_t attn_prefill_backward_workspace_size(int B, int T, int h_q) {
+    if (B <= 0 || T <= 0 || h_q <= 0) return 0;
+    const long long tpad = ((long long)T + 63) / 64 * 64;
+    return align_up((size_t)((long long)B * h_q * tpad) * 2 * sizeof(float), 256);
+}
+
+attn_status_t attn_prefill_backward(const void *q, const void *k, const void *v, const void *o,
+                                    const void *dout, const float *lse, void *dq, void *dk,
+                                    void *dv, int B, int T, int h_q, int h_kv, int d_h,
+                                    attn_dtype_t dtype, int causal, int window, float scale,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(o) || bad_ptr(dout) || bad_ptr(lse) ||
+        bad_ptr(dq) || bad_ptr(dk) || bad_ptr(dv))
+        return ATTN_ERR_INVALID_ARG;
+    if (B <= 0 || T <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
+    if (h_q % h_kv != 0) return ATTN_ERR_INVALID_ARG;
+    if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+    if (dtype != ATTN_BF16 || d_h != 128) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * h_q * (T + 63) * d_h >= (1LL << 40)) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * h_q > 65535) return ATTN_ERR_UNSUPPORTED;
+    const size_t need = attn_prefill_backward_workspace_size(B, T, h_q);
+    if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const int tpad = (T + 63) / 64 * 64;
+    mi355::PrefillBwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, T, h_q, h_kv, d_h,
+                            causal ? 1 : 0, window, scale, static_cast<float *>(workspace), tpad};
+    return mi355::launch_prefill_bwd_bf16_d128(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 static int resolve_decode_split(int split_tokens, int B, int S_max, int h_q, int h_kv) {
     if (split_tokens == 0) return default_decode_split(B, S_max, h_kv, h_q / h_kv, device_cu_count());
     return split_tokens;

@@ -21,6 +21,20 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs &a, hipStream_t stream);
 // fp32, d in {16, 32, 64, 128}, fp32 FMA.
 hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t stream);
 
+struct PrefillBwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    void *dq, *dk, *dv;
+    int B, T, hq, hkv, d;
+    int causal, window;
+    float scale;
+    float *ws_stats;      // [B * hq, Tpad, 2]: lse * log2(e) (+inf on pad rows), dout . o
+    int Tpad;             // T rounded up to a multiple of 64
+};
+// bf16, d = 128: a row-statistics pass, then dK/dV (key-block parallel)
+// and dQ (query-block parallel).
+hipError_t launch_prefill_bwd_bf16_d128(const PrefillBwdArgs &a, hipStream_t stream);
+
 struct DecodeArgs {
     const void *q, *k_cache, *v_cache;
     void *o;
