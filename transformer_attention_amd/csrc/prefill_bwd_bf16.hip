@@ -34,6 +34,8 @@
 //  (r / 4) mod 4 16-byte slots: both the 16-byte row reads of a quarter wave
 //  (16 consecutive rows, one chunk) and the transposing reads of a half wave
 //  (4 rows x 64 bytes) then hit 16 distinct slots, i.e. no bank conflicts.
+#include <type_traits>
+
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -222,6 +224,112 @@ void bwd_dkdv_kernel(Params p) {
     };
 
     const float c = p.c;
+    // One 64-row Q / dO tile against this wave's 32 keys (MASKED: some pair
+    // of the tile is not visible, or rows pass T), one 32-row block at a
+    // time.  S, dP accumulate in VGPRs and dK^T, dV^T stay pinned in AGPRs
+    // (asm MFMAs that carry their own wait states: mfma_s_first /
+    // mfma_s_last / mfma_o_acc), so the compiler never moves the output
+    // accumulators through VGPRs.
+    auto step_rows = [&](auto masked, const char *qtile, const char *gtile, const char *stat,
+                         int r0) {
+        constexpr bool MASKED = decltype(masked)::value;
+        // (not unrolled: one block at a time keeps the live registers of a
+        // single block)
+#pragma unroll 1
+        for (int mb = 0; mb < 2; ++mb) {
+            // S = Q K^T and dP = dO V^T for tile rows 32 mb .. 32 mb + 31
+            // (operands are loaded SPF k-steps ahead of their MFMAs)
+            constexpr int SPF = 2;
+            f32x16 sacc, pacc;
+            bf16x8 aqs[SPF + 1], ags[SPF + 1];
+            const char *qrow = qtile + toff(32 * mb + l32, hi);
+            const char *grow = gtile + toff(32 * mb + l32, hi);
+#pragma unroll
+            for (int i = 0; i < SPF; ++i) {
+                aqs[i] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * i);
+                ags[i] = *reinterpret_cast<const bf16x8 *>(grow + 32 * i);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                if (ks + SPF < 8) {
+                    aqs[(ks + SPF) % (SPF + 1)] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * (ks + SPF));
+                    ags[(ks + SPF) % (SPF + 1)] = *reinterpret_cast<const bf16x8 *>(grow + 32 * (ks + SPF));
+                }
+                const bf16x8 aq = aqs[ks % (SPF + 1)];
+                const bf16x8 ag = ags[ks % (SPF + 1)];
+                if (ks == 0) {
+                    sacc = mfma_s_first(aq, kop[0]);
+                    pacc = mfma_s_first(ag, vop[0]);
+                } else if (ks < 7) {
+                    sacc = mfma_s_acc(aq, kop[ks], sacc);
+                    pacc = mfma_s_acc(ag, vop[ks], pacc);
+                } else {
+                    sacc = mfma_s_acc(aq, kop[7], sacc);
+                    pacc = mfma_s_last(ag, vop[7], pacc);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // element i: tile row 32 mb + 8 (i / 4) + 4 hi + (i % 4), key `key`;
+            // st[i/2] holds (L, D) of rows 2(i/2) and 2(i/2)+1 of that pattern
+            f32x4 st[8];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int row = 32 * mb + 8 * gq + 4 * hi;
+                st[2 * gq] = *reinterpret_cast<const f32x4 *>(stat + 8 * row);
+                st[2 * gq + 1] = *reinterpret_cast<const f32x4 *>(stat + 8 * row + 16);
+            }
+            float pv[16], dsv[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float l2e = st[i >> 1][2 * (i & 1)];
+                const float dde = st[i >> 1][2 * (i & 1) + 1];
+                float pe = fast_exp2(__builtin_fmaf(sacc[i], c, -l2e));
+                float de = pe * (pacc[i] - dde);
+                if constexpr (MASKED) {
+                    const int qi = r0 + 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
+                    bool vis = qi < T;
+                    if (p.causal) vis = vis && key <= qi;
+                    if (p.window > 0) vis = vis && qi - key < p.window;
+                    pe = vis ? pe : 0.f;
+                    de = vis ? de : 0.f;
+                }
+                pv[i] = pe;
+                dsv[i] = de;
+            }
+            bf16x8 pb[2], sb[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                pb[hf] = to_bf16x8(pv[8 * hf], pv[8 * hf + 1], pv[8 * hf + 2], pv[8 * hf + 3],
+                                   pv[8 * hf + 4], pv[8 * hf + 5], pv[8 * hf + 6], pv[8 * hf + 7]);
+                sb[hf] = to_bf16x8(dsv[8 * hf], dsv[8 * hf + 1], dsv[8 * hf + 2], dsv[8 * hf + 3],
+                                   dsv[8 * hf + 4], dsv[8 * hf + 5], dsv[8 * hf + 6], dsv[8 * hf + 7]);
+            }
+            // the B operands were just written by VALU: 5 wait states before
+            // the first asm MFMA reads them
+            asm volatile("s_nop 4" : "+v"(pb[0]), "+v"(pb[1]), "+v"(sb[0]), "+v"(sb[1]));
+            // dV^T += dO^T P and dK^T += Q^T dS over these 32 rows (two 16-row
+            // halves); step j = (hf, db), operands loaded TPF steps ahead
+            constexpr int TPF = 2;
+            bf16x8 tg[TPF + 1], tq[TPF + 1];
+#pragma unroll
+            for (int i = 0; i < TPF; ++i) {
+                tg[i] = tr_operand(gtile, 32 * mb + 16 * (i >> 2), i & 3);
+                tq[i] = tr_operand(qtile, 32 * mb + 16 * (i >> 2), i & 3);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j + TPF < 8) {
+                    const int jn = j + TPF;
+                    tg[jn % (TPF + 1)] = tr_operand(gtile, 32 * mb + 16 * (jn >> 2), jn & 3);
+                    tq[jn % (TPF + 1)] = tr_operand(qtile, 32 * mb + 16 * (jn >> 2), jn & 3);
+                }
+                const int hf = j >> 2, db = j & 3;
+                mfma_o_acc(tg[j % (TPF + 1)], pb[hf], dvacc[db]);
+                mfma_o_acc(tq[j % (TPF + 1)], sb[hf], dkacc[db]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
     // ---- ring: steps 0 .. NSTAGE-2 in flight ----
 #pragma unroll
     for (int i = 0; i < KA_NSTAGE - 1; ++i)
@@ -244,65 +352,13 @@ void bwd_dkdv_kernel(Params p) {
         const char *qtile = smem + (s % KA_NSTAGE) * KA_STAGE;
         const char *gtile = qtile + TBYTES;
         const char *stat = gtile + TBYTES;
+        if (need_mask) step_rows(std::true_type{}, qtile, gtile, stat, r0);
+        else step_rows(std::false_type{}, qtile, gtile, stat, r0);
+    }
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            // S = Q K^T and dP = dO V^T for tile rows 32 mb .. 32 mb + 31
-            f32x16 sacc, pacc;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; pacc[i] = 0.f; }
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(qtile + toff(32 * mb + l32, 2 * ks + hi));
-                const bf16x8 ag = *reinterpret_cast<const bf16x8 *>(gtile + toff(32 * mb + l32, 2 * ks + hi));
-                sacc = mfma32x32x16(aq, kop[ks], sacc);
-                pacc = mfma32x32x16(ag, vop[ks], pacc);
-            }
-            // element i: tile row 32 mb + 8 (i / 4) + 4 hi + (i % 4), key `key`;
-            // st[i/2] holds (L, D) of rows 2(i/2) and 2(i/2)+1 of that pattern
-            f32x4 st[8];
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int row = 32 * mb + 8 * gq + 4 * hi;
-                st[2 * gq] = *reinterpret_cast<const f32x4 *>(stat + 8 * row);
-                st[2 * gq + 1] = *reinterpret_cast<const f32x4 *>(stat + 8 * row + 16);
-            }
-            float pv[16], dsv[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float l2e = st[i >> 1][2 * (i & 1)];
-                const float dde = st[i >> 1][2 * (i & 1) + 1];
-                float pe = fast_exp2(__builtin_fmaf(sacc[i], c, -l2e));
-                float de = pe * (pacc[i] - dde);
-                if (need_mask) {
-                    const int qi = r0 + 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    bool vis = qi < T;
-                    if (p.causal) vis = vis && key <= qi;
-                    if (p.window > 0) vis = vis && qi - key < p.window;
-                    pe = vis ? pe : 0.f;
-                    de = vis ? de : 0.f;
-                }
-                pv[i] = pe;
-                dsv[i] = de;
-            }
-            bf16x8 pb[2], sb[2];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                pb[hf] = to_bf16x8(pv[8 * hf], pv[8 * hf + 1], pv[8 * hf + 2], pv[8 * hf + 3],
-                                   pv[8 * hf + 4], pv[8 * hf + 5], pv[8 * hf + 6], pv[8 * hf + 7]);
-                sb[hf] = to_bf16x8(dsv[8 * hf], dsv[8 * hf + 1], dsv[8 * hf + 2], dsv[8 * hf + 3],
-                                   dsv[8 * hf + 4], dsv[8 * hf + 5], dsv[8 * hf + 6], dsv[8 * hf + 7]);
-            }
-            // dV^T += dO^T P and dK^T += Q^T dS over these 32 rows (two 16-row halves)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    const bf16x8 ag = tr_operand(gtile, 32 * mb + 16 * hf, db);
-                    dvacc[db] = mfma32x32x16(ag, pb[hf], dvacc[db]);
-                    const bf16x8 aq = tr_operand(qtile, 32 * mb + 16 * hf, db);
-                    dkacc[db] = mfma32x32x16(aq, sb[hf], dkacc[db]);
-                }
-        }
+    for (int db = 0; db < 4; ++db) {
+        settle_acc(dkacc[db]);
+        settle_acc(dvacc[db]);
     }
 
     // dK^T / dV^T element i of d-block db: d = 32 db + 8 (i / 4) + 4 hi + (i % 4), key `key`
