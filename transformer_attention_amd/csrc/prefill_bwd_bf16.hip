@@ -183,9 +183,15 @@ void bwd_dkdv_kernel(Params p) {
         }
     }
     const uint32_t smem_lds = lds_offset(smem);
+    // Steps run over (query tile, head) with the head fastest and the tiles
+    // from the last one down: every key block of a K/V head then reads the
+    // same Q / dO tile at the same time (they only differ in where they
+    // stop), so the tiles are shared through the XCD's L2.
+    int is_h = 0, is_qt = qt_end - 1;           // next step to copy
     auto issue_step = [&](int s) {
-        const int h = g * p.G + s / nq;
-        const int qt = qt_beg + s % nq;
+        const int h = g * p.G + is_h;
+        const int qt = is_qt;
+        if (++is_h == p.G) { is_h = 0; --is_qt; }
         const int r0 = qt * TROWS;
         const size_t bh = (size_t)b * p.hq + h;
         const __bf16 *qb = p.q + (bh * T + r0) * D;
@@ -242,6 +248,10 @@ void bwd_dkdv_kernel(Params p) {
             constexpr int SPF = 2;
             f32x16 sacc, pacc;
             bf16x8 aqs[SPF + 1], ags[SPF + 1];
+            // element i: tile row 32 mb + 8 (i / 4) + 4 hi + (i % 4), key `key`;
+            // st[i/2] holds (L, D) of rows 2(i/2) and 2(i/2)+1 of that pattern
+            // (read under the last score MFMAs)
+            f32x4 st[8];
             const char *qrow = qtile + toff(32 * mb + l32, hi);
             const char *grow = gtile + toff(32 * mb + l32, hi);
 #pragma unroll
@@ -267,16 +277,15 @@ void bwd_dkdv_kernel(Params p) {
                     sacc = mfma_s_acc(aq, kop[7], sacc);
                     pacc = mfma_s_last(ag, vop[7], pacc);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // element i: tile row 32 mb + 8 (i / 4) + 4 hi + (i % 4), key `key`;
-            // st[i/2] holds (L, D) of rows 2(i/2) and 2(i/2)+1 of that pattern
-            f32x4 st[8];
+                if (ks == 5) {
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int row = 32 * mb + 8 * gq + 4 * hi;
-                st[2 * gq] = *reinterpret_cast<const f32x4 *>(stat + 8 * row);
-                st[2 * gq + 1] = *reinterpret_cast<const f32x4 *>(stat + 8 * row + 16);
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int row = 32 * mb + 8 * gq + 4 * hi;
+                        st[2 * gq] = *reinterpret_cast<const f32x4 *>(stat + 8 * row);
+                        st[2 * gq + 1] = *reinterpret_cast<const f32x4 *>(stat + 8 * row + 16);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
             float pv[16], dsv[16];
 #pragma unroll
@@ -335,13 +344,14 @@ void bwd_dkdv_kernel(Params p) {
     for (int i = 0; i < KA_NSTAGE - 1; ++i)
         if (i < n_steps) issue_step(i);
 
+    int cs_h = 0, cs_qt = qt_end - 1;           // step being computed
     for (int s = 0; s < n_steps; ++s) {
         wait_steps(min(KA_NSTAGE - 2, n_steps - 1 - s));
         raw_barrier();                           // step s landed everywhere; step s-1 done
         if (s + KA_NSTAGE - 1 < n_steps) issue_step(s + KA_NSTAGE - 1);
 
-        const int qt = qt_beg + s % nq;
-        const int r0 = qt * TROWS;
+        const int r0 = cs_qt * TROWS;
+        if (++cs_h == p.G) { cs_h = 0; --cs_qt; }
         // does any row of the tile see any key of this wave?
         const bool active = kw0 < T && (!p.causal || r0 + TROWS - 1 >= kw0) &&
                             (p.window <= 0 || r0 <= kw0 + 31 + p.window - 1);
