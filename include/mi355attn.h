@@ -179,6 +179,51 @@ attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *ls
                          void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/*
+ * Paged KV caches -- the same two decode steps with the cache held in
+ * fixed-size pages that a per-sequence block table maps to, the layout of
+ * production serving engines ("Attention deep dive ...", section 5 "The KV
+ * cache", the production-engine notes: pages remove fragmentation and let
+ * sequences of different lengths share memory; "2.4 Multi-Head Attention,
+ * MQA, GQA & MLA", GQA in the real libraries: paged blocks sized from the
+ * K/V head count).  Only the addressing changes: the result is the
+ * contiguous decode's on the gathered cache.
+ *
+ *   k_pages, v_pages : [num_pages, h_kv, page_size, d_h]  bf16 (read)
+ *   kv_pages (MLA)   : [num_pages, page_size, d_c + d_r]   bf16 (read)
+ *   block_table      : [B, max_blocks] int32, device memory: position t of
+ *                      sequence b is row t % page_size of page
+ *                      block_table[b * max_blocks + t / page_size].  Only the
+ *                      entries of positions < seq_lens[b] are read; an entry
+ *                      outside [0, num_pages) is clamped into it (no fault,
+ *                      wrong data).
+ *   seq_lens         : as for the contiguous calls, clamped to
+ *                      [0, max_blocks * page_size].
+ * Everything else (q, o, lse, window, scale, split_tokens, workspace,
+ * errors) is as in attn_decode / mla_decode with S_max = max_blocks *
+ * page_size; the *_paged_workspace_size functions return exactly that.
+ * page_size must be a positive multiple of 32 (ATTN_ERR_UNSUPPORTED
+ * otherwise); a null block_table or non-positive max_blocks, page_size or
+ * num_pages is ATTN_ERR_INVALID_ARG.
+ */
+size_t attn_decode_paged_workspace_size(int B, int max_blocks, int page_size, int h_q,
+                                        int h_kv, int d_h, int split_tokens);
+attn_status_t attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                                void *o, float *lse, const int32_t *seq_lens,
+                                const int32_t *block_table, int B, int max_blocks,
+                                int page_size, int num_pages, int h_q, int h_kv, int d_h,
+                                int window, float scale, int split_tokens,
+                                void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+size_t mla_decode_paged_workspace_size(int B, int max_blocks, int page_size, int h_q,
+                                       int d_c, int d_r, int split_tokens);
+attn_status_t mla_decode_paged(const void *q, const void *kv_pages, void *o, float *lse,
+                               const int32_t *seq_lens, const int32_t *block_table,
+                               int B, int max_blocks, int page_size, int num_pages,
+                               int h_q, int d_c, int d_r, float scale, int split_tokens,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *attn_status_string(attn_status_t status);
 

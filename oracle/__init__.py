@@ -190,6 +190,47 @@ def mla_decode(q, cache, seq_lens, *, d_c: int, d_r: int, scale: float):
     return o, lse
 
 
+def gather_pages(pages, block_table, seq_lens, *, head_axis: bool):
+    """Contiguous cache from a paged one: position t of sequence b is row
+    t % page_size of page block_table[b, t // page_size].  pages is
+    [num_pages, h_kv, page_size, d] (head_axis) or [num_pages, page_size, d];
+    returns [B, h_kv, S_max, d] or [B, S_max, d] with S_max = max_blocks *
+    page_size; positions at or past seq_lens[b] are left at zero."""
+    pages = np.asarray(pages)
+    bt = np.asarray(block_table)
+    lens = np.asarray(seq_lens)
+    B, max_blocks = bt.shape
+    ps = pages.shape[2] if head_axis else pages.shape[1]
+    S_max = max_blocks * ps
+    if head_axis:
+        out = np.zeros((B, pages.shape[1], S_max, pages.shape[3]), dtype=pages.dtype)
+    else:
+        out = np.zeros((B, S_max, pages.shape[2]), dtype=pages.dtype)
+    for b in range(B):
+        n = int(min(max(int(lens[b]), 0), S_max))
+        for t0 in range(0, n, ps):
+            pg = int(bt[b, t0 // ps])
+            m = min(ps, n - t0)
+            if head_axis:
+                out[b, :, t0:t0 + m] = pages[pg, :, :m]
+            else:
+                out[b, t0:t0 + m] = pages[pg, :m]
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, *, window: int = 0, scale: float):
+    """attn decode on a paged cache: the contiguous decode of the gathered cache."""
+    kc = gather_pages(_f32(k_pages), block_table, seq_lens, head_axis=True)
+    vc = gather_pages(_f32(v_pages), block_table, seq_lens, head_axis=True)
+    return decode(q, kc, vc, seq_lens, window=window, scale=scale)
+
+
+def mla_decode_paged(q, kv_pages, block_table, seq_lens, *, d_c: int, d_r: int, scale: float):
+    """MLA decode on a paged cache: the contiguous MLA decode of the gathered cache."""
+    c = gather_pages(_f32(kv_pages), block_table, seq_lens, head_axis=False)
+    return mla_decode(q, c, seq_lens, d_c=d_c, d_r=d_r, scale=scale)
+
+
 def merge_partials(parts_o, parts_lse):
     """Merge normalised partial results over disjoint key sets.
     parts_o:[n,dv] parts_lse:[n] -> (o:[dv], lse)."""

@@ -32,6 +32,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("attn_prefill", "attn_prefill_backward", "attn_prefill_backward_workspace_size",
               "attn_decode", "mla_decode", "attn_decode_workspace_size",
+              "attn_decode_paged", "attn_decode_paged_workspace_size", "mla_decode_paged",
+              "mla_decode_paged_workspace_size",
               "mla_decode_workspace_size", "attn_status_string", "attn_abi_version"):
         assert n in names, n
 
@@ -120,6 +122,42 @@ def test_decode_validation(lib):
     assert need > 0
     assert dec(wsb=need - 1) == 3
     assert lib.attn_decode_workspace_size(2, 64, 7, 2, 128, 0) == 0
+
+
+def test_paged_validation(lib):
+    def dec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lens=FAKE, bt=FAKE, B=2, mb=8, ps=64, np_=16,
+                 hq=8, hkv=2, d=128, window=0, scale=0.1, split=0, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.attn_decode_paged(a["q"], a["k"], a["v"], a["o"], None, a["lens"], a["bt"],
+                                     a["B"], a["mb"], a["ps"], a["np_"], a["hq"], a["hkv"], a["d"],
+                                     a["window"], a["scale"], a["split"], a["ws"], a["wsb"], None)
+    assert dec(bt=None) == 1
+    assert dec(mb=0) == 1
+    assert dec(np_=0) == 1
+    assert dec(ps=0) == 1
+    assert dec(ps=48) == 2                          # pages are multiples of 32 positions
+    assert dec(hq=7) == 1
+    assert dec(d=64) == 2
+    assert dec(ws=None) == 3
+    need = lib.attn_decode_paged_workspace_size(2, 8, 64, 8, 2, 128, 0)
+    assert need == lib.attn_decode_workspace_size(2, 512, 8, 2, 128, 0) > 0
+    assert dec(wsb=need - 1) == 3
+
+    def mla(**kw):
+        a = dict(q=FAKE, c=FAKE, o=FAKE, lens=FAKE, bt=FAKE, B=2, mb=4, ps=64, np_=8, H=128,
+                 dc=512, dr=64, scale=0.1, split=0, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.mla_decode_paged(a["q"], a["c"], a["o"], None, a["lens"], a["bt"], a["B"],
+                                    a["mb"], a["ps"], a["np_"], a["H"], a["dc"], a["dr"],
+                                    a["scale"], a["split"], a["ws"], a["wsb"], None)
+    assert mla(bt=None) == 1
+    assert mla(ps=100) == 2
+    assert mla(dc=256) == 2
+    assert mla(ws=None) == 3
+    need = lib.mla_decode_paged_workspace_size(2, 4, 64, 128, 512, 64, 0)
+    assert need == lib.mla_decode_workspace_size(2, 256, 128, 512, 64, 0) > 0
+    assert mla(wsb=need - 1) == 3
 
 
 def test_mla_validation(lib):

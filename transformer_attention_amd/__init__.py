@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
               split_tokens=0, o=None, lse=None, workspace=None)
   mla_decode(q, kv_cache, seq_lens, *, d_c=512, d_r=64, scale,
              split_tokens=0, o=None, lse=None, workspace=None)
+  attn_decode_paged(q, k_pages, v_pages, seq_lens, block_table, ...)
+  mla_decode_paged(q, kv_pages, seq_lens, block_table, ...)
 """
 from __future__ import annotations
 
@@ -40,7 +42,9 @@ ATTN_BF16 = 1
 EXPORTED_SYMBOLS = (
     "attn_prefill", "attn_prefill_backward", "attn_prefill_backward_workspace_size",
     "attn_decode", "attn_decode_workspace_size",
-    "mla_decode", "mla_decode_workspace_size", "attn_status_string",
+    "mla_decode", "mla_decode_workspace_size", "attn_decode_paged",
+    "attn_decode_paged_workspace_size", "mla_decode_paged", "mla_decode_paged_workspace_size",
+    "attn_status_string",
     "attn_abi_version",
 )
 
@@ -79,6 +83,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_workspace_size.restype = Z
     lib.mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, Z, P]
     lib.mla_decode.restype = I
+    lib.attn_decode_paged_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.attn_decode_paged_workspace_size.restype = Z
+    lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.attn_decode_paged.restype = I
+    lib.mla_decode_paged_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.mla_decode_paged_workspace_size.restype = Z
+    lib.mla_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.mla_decode_paged.restype = I
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -282,4 +294,87 @@ def mla_decode(q, kv_cache, seq_lens, *, d_c: int = 512, d_r: int = 64, scale: f
                         B, S_max, H, d_c, d_r, float(scale), int(split_tokens),
                         _ptr(workspace), ws_bytes, _stream(q.device))
     _check(st, "mla_decode")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_decode_paged(q, k_pages, v_pages, seq_lens, block_table, *, window: int = 0, scale=None,
+                      split_tokens: int = 0, o=None, lse=None, workspace=None,
+                      return_lse: bool = False):
+    """q:[B,h_q,d] or [B,h_q,1,d] bf16; pages:[num_pages,h_kv,page_size,d] bf16;
+    block_table: int32[B,max_blocks] and seq_lens: int32[B] on the device."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16)
+    _require(k_pages, "k_pages", torch.bfloat16, q.device, 4)
+    _require(v_pages, "v_pages", torch.bfloat16, q.device, 4)
+    _require(seq_lens, "seq_lens", torch.int32, q.device, 1)
+    _require(block_table, "block_table", torch.int32, q.device, 2)
+    num_pages, hkv, page_size, d = k_pages.shape
+    if tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("v_pages shape mismatch")
+    B, max_blocks = block_table.shape
+    hq = q.shape[1]
+    if q.numel() != B * hq * d or q.shape[0] != B or q.shape[-1] != d:
+        raise ValueError("q shape mismatch")
+    if seq_lens.shape[0] != B:
+        raise ValueError("seq_lens shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    _require(o, "o", torch.bfloat16, q.device)
+    if o.numel() != q.numel():
+        raise ValueError("o shape mismatch")
+    if lse is None and return_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, q.device)
+    need = lib.attn_decode_paged_workspace_size(B, max_blocks, page_size, hq, hkv, d,
+                                                int(split_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", None, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), _ptr(lse),
+                               _ptr(seq_lens), _ptr(block_table), B, max_blocks, page_size,
+                               num_pages, hq, hkv, d, int(window), float(scale),
+                               int(split_tokens), _ptr(workspace), ws_bytes, _stream(q.device))
+    _check(st, "attn_decode_paged")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def mla_decode_paged(q, kv_pages, seq_lens, block_table, *, d_c: int = 512, d_r: int = 64,
+                     scale: float, split_tokens: int = 0, o=None, lse=None, workspace=None,
+                     return_lse: bool = False):
+    """q:[B,H,d_c+d_r] bf16; kv_pages:[num_pages,page_size,d_c+d_r] bf16;
+    block_table: int32[B,max_blocks] and seq_lens: int32[B] on the device."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16, ndim=3)
+    _require(kv_pages, "kv_pages", torch.bfloat16, q.device, 3)
+    _require(seq_lens, "seq_lens", torch.int32, q.device, 1)
+    _require(block_table, "block_table", torch.int32, q.device, 2)
+    B, H, dk = q.shape
+    num_pages, page_size, dk2 = kv_pages.shape
+    if dk != d_c + d_r or dk2 != dk or block_table.shape[0] != B:
+        raise ValueError("q / kv_pages / block_table shape mismatch")
+    max_blocks = block_table.shape[1]
+    if o is None:
+        o = torch.empty((B, H, d_c), dtype=torch.bfloat16, device=q.device)
+    _require(o, "o", torch.bfloat16, q.device)
+    if o.numel() != B * H * d_c:
+        raise ValueError("o shape mismatch")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, q.device)
+    need = lib.mla_decode_paged_workspace_size(B, max_blocks, page_size, H, d_c, d_r,
+                                               int(split_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", None, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.mla_decode_paged(_ptr(q), _ptr(kv_pages), _ptr(o), _ptr(lse), _ptr(seq_lens),
+                              _ptr(block_table), B, max_blocks, page_size, num_pages, H, d_c,
+                              d_r, float(scale), int(split_tokens), _ptr(workspace), ws_bytes,
+                              _stream(q.device))
+    _check(st, "mla_decode_paged")
     return (o, lse) if (return_lse or lse is not None) else o

@@ -164,6 +164,47 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     return mi355::launch_decode_bf16_d128(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+size_t attn_decode_paged_workspace_size(int B, int max_blocks, int page_size, int h_q, int h_kv,
+                                        int d_h, int split_tokens) {
+    if (max_blocks <= 0 || page_size <= 0 || (long long)max_blocks * page_size > 0x7fffffffLL) return 0;
+    return attn_decode_workspace_size(B, max_blocks * page_size, h_q, h_kv, d_h, split_tokens);
+}
+
+static bool bad_pages(const int32_t *block_table, int max_blocks, int page_size, int num_pages) {
+    return bad_ptr(block_table) || max_blocks <= 0 || page_size <= 0 || num_pages <= 0 ||
+           (long long)max_blocks * page_size > 0x7fffffffLL;
+}
+
+attn_status_t attn_decode_paged(const void *q, const void *k_pages, const void *v_pages, void *o,
+                                float *lse, const int32_t *seq_lens, const int32_t *block_table,
+                                int B, int max_blocks, int page_size, int num_pages, int h_q,
+                                int h_kv, int d_h, int window, float scale, int split_tokens,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (bad_ptr(q) || bad_ptr(k_pages) || bad_ptr(v_pages) || bad_ptr(o) || bad_ptr(seq_lens))
+        return ATTN_ERR_INVALID_ARG;
+    if (bad_pages(block_table, max_blocks, page_size, num_pages)) return ATTN_ERR_INVALID_ARG;
+    if (B <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
+    if (h_q % h_kv != 0 || window < 0 || !isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+    if (split_tokens < 0 || split_tokens % 64) return ATTN_ERR_INVALID_ARG;
+    if (page_size % 32) return ATTN_ERR_UNSUPPORTED;
+    if (d_h != 128) return ATTN_ERR_UNSUPPORTED;
+    if (B > 65535 || h_kv * ((h_q / h_kv + 15) / 16) > 65535) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * max_blocks > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+    const int S_max = max_blocks * page_size;
+    const int split = resolve_decode_split(split_tokens, B, S_max, h_q, h_kv);
+    const int ns = (S_max + split - 1) / split;
+    const size_t need = attn_decode_workspace_size(B, S_max, h_q, h_kv, d_h, split_tokens);
+    if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    float *ws_o = static_cast<float *>(workspace);
+    char *ws_end = static_cast<char *>(workspace) + align_up((size_t)B * h_q * ns * d_h * sizeof(float), 256);
+    float *ws_lse = reinterpret_cast<float *>(ws_end);
+    int32_t *plan = reinterpret_cast<int32_t *>(ws_end + align_up((size_t)B * h_q * ns * sizeof(float), 256));
+    mi355::DecodeArgs a{q, k_pages, v_pages, o, lse, seq_lens, B, S_max, h_q, h_kv, d_h,
+                        window, scale, split, ns, ws_o, ws_lse, plan, device_cu_count(),
+                        block_table, max_blocks, page_size, num_pages};
+    return mi355::launch_decode_bf16_d128(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 size_t mla_decode_workspace_size(int B, int S_max, int h_q, int d_c, int d_r, int split_tokens) {
     if (B <= 0 || S_max <= 0 || h_q <= 0 || d_c <= 0 || d_r < 0) return 0;
     if (split_tokens < 0 || split_tokens % 64) return 0;
@@ -191,6 +232,38 @@ attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *ls
                                               align_up((size_t)B * h_q * ns * d_c * sizeof(float), 256));
     mi355::MlaArgs a{q, kv_cache, o, lse, seq_lens, B, S_max, h_q, d_c, d_r, scale, split, ns,
                      ws_o, ws_lse};
+    return mi355::launch_mla_decode_bf16(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t mla_decode_paged_workspace_size(int B, int max_blocks, int page_size, int h_q, int d_c,
+                                       int d_r, int split_tokens) {
+    if (max_blocks <= 0 || page_size <= 0 || (long long)max_blocks * page_size > 0x7fffffffLL) return 0;
+    return mla_decode_workspace_size(B, max_blocks * page_size, h_q, d_c, d_r, split_tokens);
+}
+
+attn_status_t mla_decode_paged(const void *q, const void *kv_pages, void *o, float *lse,
+                               const int32_t *seq_lens, const int32_t *block_table, int B,
+                               int max_blocks, int page_size, int num_pages, int h_q, int d_c,
+                               int d_r, float scale, int split_tokens, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    if (bad_ptr(q) || bad_ptr(kv_pages) || bad_ptr(o) || bad_ptr(seq_lens)) return ATTN_ERR_INVALID_ARG;
+    if (bad_pages(block_table, max_blocks, page_size, num_pages)) return ATTN_ERR_INVALID_ARG;
+    if (B <= 0 || h_q <= 0 || d_c <= 0 || d_r < 0) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f) || split_tokens < 0 || split_tokens % 64)
+        return ATTN_ERR_INVALID_ARG;
+    if (page_size % 32) return ATTN_ERR_UNSUPPORTED;
+    if (d_c != 512 || d_r != 64 || h_q % 16 != 0) return ATTN_ERR_UNSUPPORTED;
+    if (B > 65535 || (long long)B * max_blocks > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+    const int S_max = max_blocks * page_size;
+    const int split = split_tokens ? split_tokens : default_mla_split(B, S_max, h_q);
+    const int ns = (S_max + split - 1) / split;
+    const size_t need = mla_decode_workspace_size(B, S_max, h_q, d_c, d_r, split_tokens);
+    if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    float *ws_o = static_cast<float *>(workspace);
+    float *ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                              align_up((size_t)B * h_q * ns * d_c * sizeof(float), 256));
+    mi355::MlaArgs a{q, kv_pages, o, lse, seq_lens, B, S_max, h_q, d_c, d_r, scale, split, ns,
+                     ws_o, ws_lse, block_table, max_blocks, page_size, num_pages};
     return mi355::launch_mla_decode_bf16(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -66,6 +66,11 @@ constexpr float TAU = 8.0f;
 struct Params {
     const __bf16 *q, *k, *v;
     const int32_t *seq_lens;
+    // paged cache: k and v are [num_pages, h_kv, page_size, D]; position t of
+    // sequence b is row t % page_size of page block_table[b * max_blocks +
+    // t / page_size] (entries clamped to [0, num_pages - 1])
+    const int32_t *block_table;
+    int max_blocks, page_size, num_pages;
     const int32_t *plan;                  // [B+1] unit prefix sums
     float *ws_o, *ws_lse;
     int B, S_max, hq, hkv, G, n_hchunk;
@@ -106,9 +111,14 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *seq_le
 struct Unit {
     int b, g, hc, c;      // sequence, K/V head, head chunk, chunk index
     int lo, hi;           // visible key range of the chunk
+    int t_first;          // first key of the first tile (lo, or lo rounded down to 32 when paged)
     int n_tiles;
 };
 
+// PAGED: the tiles of a chunk start on 32-key boundaries, so that a tile
+// never straddles two pages (page sizes are multiples of 32); keys before
+// the visible start of the first tile are masked.
+template <bool PAGED>
 __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x;
@@ -153,7 +163,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         const int kvis = p.window > 0 ? max(0, len - p.window) : 0;
         d.lo = max(d.c * p.split, kvis);
         d.hi = min((d.c + 1) * p.split, len);
-        d.n_tiles = d.lo < d.hi ? (d.hi - d.lo + BN - 1) / BN : 0;
+        d.t_first = PAGED ? (d.lo & ~(BN - 1)) : d.lo;
+        d.n_tiles = d.lo < d.hi ? (d.hi - d.t_first + BN - 1) / BN : 0;
         return d;
     };
 
@@ -199,10 +210,17 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
     auto issue_next = [&]() {                        // issue the fetch cursor's tile
         fetch_skip_empty();
         if (fu >= total) return false;
-        const size_t kv_base = ((size_t)fd.b * p.hkv + fd.g) * (size_t)p.S_max * D;
-        const int t0 = fd.lo + ft * BN;
-        const char *kg = reinterpret_cast<const char *>(p.k + kv_base + (size_t)t0 * D);
-        const char *vg = reinterpret_cast<const char *>(p.v + kv_base + (size_t)t0 * D);
+        const int t0 = fd.t_first + ft * BN;
+        size_t row0;                             // element offset of the tile's first row
+        if constexpr (PAGED) {
+            int pg = ld_uniform(p.block_table, fd.b * p.max_blocks + t0 / p.page_size);
+            pg = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+            row0 = (((size_t)pg * p.hkv + fd.g) * p.page_size + (t0 % p.page_size)) * D;
+        } else {
+            row0 = (((size_t)fd.b * p.hkv + fd.g) * (size_t)p.S_max + t0) * D;
+        }
+        const char *kg = reinterpret_cast<const char *>(p.k + row0);
+        const char *vg = reinterpret_cast<const char *>(p.v + row0);
         const uint32_t stage = ring_lds + (nf % NSTG) * STAGE_BYTES;
         vmc += STAGE_BLK;
         vm_prev = vm_last;
@@ -283,7 +301,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
             // this tile is the nc_done-th fetched; a later one may be in flight
             wait_after(nc_done == nf - 1 ? vm_last : vm_prev);   // this tile's copies landed
             const char *st = ring + (nc_done % NSTG) * STAGE_BYTES;
-            const int t0 = d.lo + j * BN;
+            const int t0 = d.t_first + j * BN;
             bf16x8 ka[2][4];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
@@ -305,7 +323,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
                     sacc[mb] = mfma16x16x32(ka[mb][ks], qop[ks], sacc[mb]);
                 }
             // element (mb, i) of this lane is key t0 + 16 mb + 4 q16 + i of head column j16
-            const bool tail = t0 + BN > d.hi;
+            const bool tail = t0 + BN > d.hi || (PAGED && t0 < d.lo);
             float x[8];
             float mx = -INFINITY;
 #pragma unroll
@@ -313,7 +331,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float v = sacc[mb][i] * p.scale_log2;
-                    if (tail) v = (t0 + 16 * mb + 4 * q16 + i < d.hi) ? v : -INFINITY;
+                    const int key = t0 + 16 * mb + 4 * q16 + i;
+                    if (tail) v = (key < d.hi && (!PAGED || key >= d.lo)) ? v : -INFINITY;
                     x[4 * mb + i] = v;
                     mx = fmaxf(mx, v);
                 }
@@ -451,6 +470,10 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
     p.k = static_cast<const __bf16 *>(a.k_cache);
     p.v = static_cast<const __bf16 *>(a.v_cache);
     p.seq_lens = a.seq_lens;
+    p.block_table = a.block_table;
+    p.max_blocks = a.max_blocks;
+    p.page_size = a.page_size;
+    p.num_pages = a.num_pages;
     p.plan = a.plan;
     p.ws_o = a.ws_o;
     p.ws_lse = a.ws_lse;
@@ -470,7 +493,10 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     static bool attr_set = false;
     if (!attr_set) {
-        e = hipFuncSetAttribute((const void *)decode_bf16_d128_kernel,
+        e = hipFuncSetAttribute((const void *)decode_bf16_d128_kernel<false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute((const void *)decode_bf16_d128_kernel<true>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
@@ -481,8 +507,12 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
     long long blocks = (max_units + NW - 1) / NW;
     if (blocks > a.num_cus) blocks = a.num_cus;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(decode_bf16_d128_kernel, dim3((unsigned)blocks), dim3(64 * NW), LDS_BYTES,
-                       stream, p);
+    if (a.block_table)
+        hipLaunchKernelGGL(decode_bf16_d128_kernel<true>, dim3((unsigned)blocks), dim3(64 * NW),
+                           LDS_BYTES, stream, p);
+    else
+        hipLaunchKernelGGL(decode_bf16_d128_kernel<false>, dim3((unsigned)blocks), dim3(64 * NW),
+                           LDS_BYTES, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_combine(a.ws_o, a.ws_lse, a.seq_lens, a.o, a.lse, a.B, a.hq, D, a.S_max,

@@ -49,6 +49,11 @@ struct DecodeArgs {
     float *ws_lse;        // [B, hq, n_split_max]  (log2 units)
     int32_t *plan;        // [B + 1] unit prefix sums (workspace)
     int num_cus;          // compute units of the device (persistent grid size)
+    // paged cache (block_table == nullptr: contiguous [B, hkv, S_max, d]):
+    // k_cache / v_cache are [num_pages, hkv, page_size, d], S_max =
+    // max_blocks * page_size
+    const int32_t *block_table;
+    int max_blocks, page_size, num_pages;
 };
 hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream);
 
@@ -63,6 +68,10 @@ struct MlaArgs {
     int n_split_max;
     float *ws_o;          // [B, H, n_split_max, d_c]
     float *ws_lse;        // [B, H, n_split_max]  (log2 units)
+    // paged cache (block_table == nullptr: contiguous [B, S_max, d_c + d_r]):
+    // cache is [num_pages, page_size, d_c + d_r], S_max = max_blocks * page_size
+    const int32_t *block_table;
+    int max_blocks, page_size, num_pages;
 };
 hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream);
 

@@ -57,6 +57,11 @@ constexpr float TAU = 8.0f;
 struct Params {
     const __bf16 *q, *c;
     const int32_t *seq_lens;
+    // paged cache: c is [num_pages, page_size, DK]; position t of sequence b
+    // is row t % page_size of page block_table[b * max_blocks + t / page_size]
+    // (entries clamped to [0, num_pages - 1])
+    const int32_t *block_table;
+    int max_blocks, page_size, num_pages;
     float *ws_o, *ws_lse;
     int B, S_max, H;
     int split, n_split_max, n_hchunk;
@@ -75,6 +80,10 @@ struct Params {
 // in the loop indices.
 __device__ __forceinline__ int row_slot(int r) { return LROW_SLOTS * r + ((r >> 2) & 3); }
 
+// PAGED: tiles start at multiples of 32 tokens (chunks start at multiples of
+// the split, itself a multiple of 64), so a tile never straddles two pages
+// when the page size is a multiple of 32.
+template <bool PAGED>
 __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(Params p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -97,7 +106,7 @@ void mla_decode_kernel(Params p) {
     const int hi_tok = min(lo + p.split, len);
     const int n_tiles = (hi_tok - lo + TB - 1) / TB;
 
-    const char *cg = reinterpret_cast<const char *>(p.c + (size_t)b * p.S_max * DK);
+    const char *cg = PAGED ? nullptr : reinterpret_cast<const char *>(p.c + (size_t)b * p.S_max * DK);
 
     // Issue the DMA of tile `t` (relative) into its ring stage: this wave's
     // 1-KB blocks.  LDS slot q = (1024*blk + 16*lane) / 16 of the stage holds
@@ -121,7 +130,15 @@ void mla_decode_kernel(Params p) {
     auto issue_tile = [&](int t) {
         char *stage = smem + (t % NSTAGE) * TILE_BYTES;
         const int t0 = lo + t * TB;
-        const char *gbase = cg + (size_t)t0 * ROWB;
+        const char *gbase;
+        if constexpr (PAGED) {
+            int pg = ld_uniform(p.block_table, b * p.max_blocks + t0 / p.page_size);
+            pg = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+            gbase = reinterpret_cast<const char *>(p.c) +
+                    ((size_t)pg * p.page_size + (t0 % p.page_size)) * ROWB;
+        } else {
+            gbase = cg + (size_t)t0 * ROWB;
+        }
         const int last = hi_tok - 1 - t0;       // last valid row of this tile
         if (last >= TB - 1) {
 #pragma unroll
@@ -314,6 +331,10 @@ hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream) {
     p.q = static_cast<const __bf16 *>(a.q);
     p.c = static_cast<const __bf16 *>(a.cache);
     p.seq_lens = a.seq_lens;
+    p.block_table = a.block_table;
+    p.max_blocks = a.max_blocks;
+    p.page_size = a.page_size;
+    p.num_pages = a.num_pages;
     p.ws_o = a.ws_o;
     p.ws_lse = a.ws_lse;
     p.B = a.B;
@@ -324,15 +345,23 @@ hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream) {
     p.scale_log2 = a.scale * kLog2e;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)mla_decode_kernel,
+        hipError_t e = hipFuncSetAttribute((const void *)mla_decode_kernel<false>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute((const void *)mla_decode_kernel<true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     p.n_hchunk = (a.H + HPC - 1) / HPC;
     const long long n_wg = (long long)a.B * a.n_split_max * p.n_hchunk;
     if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)n_wg), dim3(64 * NW), LDS_BYTES, stream, p);
+    if (a.block_table)
+        hipLaunchKernelGGL(mla_decode_kernel<true>, dim3((unsigned)n_wg), dim3(64 * NW), LDS_BYTES,
+                           stream, p);
+    else
+        hipLaunchKernelGGL(mla_decode_kernel<false>, dim3((unsigned)n_wg), dim3(64 * NW), LDS_BYTES,
+                           stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_combine(a.ws_o, a.ws_lse, a.seq_lens, a.o, a.lse, a.B, a.H, DC, a.S_max,

@@ -161,3 +161,34 @@ def mla_inputs(shape: MlaShape, *, seed: int = 0, device="cpu",
     q = randn((B, H, dk), torch.bfloat16, generator=g, device=gd)
     cache = randn((B, S_max, dk), torch.bfloat16, generator=g, device=gd)
     return q.to(device), cache.to(device), lens.to(device)
+
+
+def paged_layout(cache: torch.Tensor, page_size: int, *, seed: int = 0, head_axis: bool = True,
+                 extra_pages: int = 0, fill=float("nan")):
+    """Lay a contiguous cache out in pages of `page_size` positions, in a
+    seeded random page order, the way a paged allocator scatters them.
+
+    cache: [B, h_kv, S, d] (head_axis) or [B, S, d], S a multiple of
+    page_size.  Returns (pages, block_table): pages [num_pages, h_kv,
+    page_size, d] or [num_pages, page_size, d] with num_pages = B * S /
+    page_size + extra_pages (the extra pages and nothing else hold `fill`),
+    block_table int32 [B, S / page_size] on the cache's device."""
+    if head_axis:
+        B, hkv, S, d = cache.shape
+    else:
+        B, S, d = cache.shape
+    if S % page_size:
+        raise ValueError("S must be a multiple of page_size")
+    nb = S // page_size
+    n_pages = B * nb + extra_pages
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(n_pages, generator=g)[:B * nb]
+    if head_axis:
+        blocks = cache.view(B, hkv, nb, page_size, d).permute(0, 2, 1, 3, 4).reshape(B * nb, hkv, page_size, d)
+        pages = torch.full((n_pages, hkv, page_size, d), fill, dtype=cache.dtype, device=cache.device)
+    else:
+        blocks = cache.view(B * nb, page_size, d)
+        pages = torch.full((n_pages, page_size, d), fill, dtype=cache.dtype, device=cache.device)
+    pages[perm.to(cache.device)] = blocks
+    table = perm.view(B, nb).to(torch.int32).to(cache.device)
+    return pages, table
