@@ -10,9 +10,10 @@ decode (B=64, 64/8 heads, cached lengths uniform in [4096, 32768]) and
 DeepSeek-V3-shaped MLA absorbed decode (B=32, 128 heads, 16384 tokens of
 576 values) -- in KV-cache GB/s, counting only cache rows inside each
 sequence plus q and o -- the two sliding-window prefills (B=4, T=4096,
-32 query heads, window 1024, with 32 and with 1 K/V head) in TFLOP/s, and
-the backward (dQ, dK, dV) of the Llama-3-8B prefill in TFLOP/s, counting
-10*d_h FLOP per visible pair (five products).
+32 query heads, window 1024, with 32 and with 1 K/V head) in TFLOP/s, the
+backward (dQ, dK, dV) of the Llama-3-8B prefill in TFLOP/s, counting
+10*d_h FLOP per visible pair (five products), and the 70B decode on a paged
+cache (pages of 64 positions in a random order) in GB/s.
 
 Inputs are seeded synthetic N(0,1) tensors (workloads.py), resident in HBM
 before timing.  W untimed warm-up steps, then exactly K timed steps between
@@ -20,7 +21,7 @@ two device synchronisations; kernel durations come from HIP events recorded
 on the stream the kernels run on.  One JSON line is printed.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|backward|decode|mla|swa-mha|swa-mqa|copy]
+                    [--only prefill|backward|decode|decode-paged|mla|swa-mha|swa-mqa|copy]
 
 ``--only copy`` times a plain 1 GiB device copy instead: it is the
 calibration run for rocprofv3's HBM byte counters, not an attention bench.
@@ -133,6 +134,32 @@ def bench_decode(torch, ta, W, steps, warmup):
             "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
+def bench_decode_paged(torch, ta, W, steps, warmup, page_size=64):
+    """The 70B decode with its cache in pages of `page_size` positions, in a
+    seeded random page order (the same bytes as the contiguous decode)."""
+    s = W.GQA70B_DECODE
+    q, kc, vc, lens = W.decode_inputs(s, seed=0, device="cuda", gen_device="cuda")
+    kp, table = W.paged_layout(kc, page_size, seed=9, fill=0.0)
+    del kc
+    vp = torch.empty_like(kp)
+    vp[table.view(-1).long()] = vc.view(s.B, s.h_kv, s.S_max // page_size, page_size, s.d_h).permute(
+        0, 2, 1, 3, 4).reshape(-1, s.h_kv, page_size, s.d_h)
+    del vc
+    lens_d = lens.to("cuda")
+    o = torch.empty_like(q)
+    ws = torch.empty(ta.attn_decode_workspace_size(s.B, s.S_max, s.h_q, s.h_kv, s.d_h),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = lambda: ta.attn_decode_paged(q, kp, vp, lens_d, table, scale=s.scale, o=o, workspace=ws)
+    ms, wall = _events_time(torch, fn, steps, warmup, stream)
+    total_len = int(lens.sum())
+    nbytes = total_len * 2 * s.h_kv * s.d_h * 2 + 2 * s.B * s.h_q * s.d_h * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del q, kp, vp, o, ws
+    return {"ms": ms, "wall_s": wall, "bytes": nbytes, "gbs": gbs, "page_size": page_size,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+
+
 def bench_copy(torch, steps, warmup, nbytes=1 << 30):
     """A plain device-to-device copy of known size (reads and writes nbytes
     each).  Not part of the attention path: its HBM counter readings give the
@@ -212,8 +239,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    choices=["prefill", "backward", "decode", "mla", "swa-mha", "swa-mqa",
-                             "copy"])
+                    choices=["prefill", "backward", "decode", "decode-paged", "mla", "swa-mha",
+                             "swa-mqa", "copy"])
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -251,6 +278,10 @@ def main(argv=None):
         out["decode"] = bench_decode(torch, ta, W, args.steps, args.warmup)
         print(f"[bench] decode {out['decode']['ms']:.3f} ms {out['decode']['gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
+    if only in (None, "decode-paged"):
+        out["decode_paged"] = bench_decode_paged(torch, ta, W, args.steps, args.warmup)
+        print(f"[bench] decode (paged) {out['decode_paged']['ms']:.3f} ms "
+              f"{out['decode_paged']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     if only in (None, "mla"):
         out["mla"] = bench_mla(torch, ta, W, args.steps, args.warmup)
         print(f"[bench] mla {out['mla']['ms']:.3f} ms {out['mla']['gbs']:.0f} GB/s",
@@ -301,6 +332,12 @@ def main(argv=None):
             r = out[key]
             line[key] = {"workload": name, "ms": round(r["ms"], 4), "TFLOP_s": round(r["tflops"], 2),
                          "frac_bf16_peak": round(r["frac_bf16_peak"], 4), "flops": r["flops"]}
+    if "decode_paged" in out and next(iter(out)) != "decode_paged":
+        d = out["decode_paged"]
+        line["decode_paged"] = {"workload": "70B-shaped GQA decode, cache in pages of "
+                                            f"{d['page_size']} positions (random page order)",
+                                "ms": round(d["ms"], 4), "GB_s": round(d["gbs"], 1),
+                                "frac_hbm_peak": round(d["frac_hbm_peak"], 4), "bytes": d["bytes"]}
     if "backward" in out and next(iter(out)) != "backward":
         r = out["backward"]
         line["backward"] = {"workload": "Llama-3-8B-shaped causal GQA prefill backward (dQ, dK, dV)",
