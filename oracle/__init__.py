@@ -63,13 +63,13 @@ def _load():
     P = ctypes.c_void_p
     I = ctypes.c_int
     D = ctypes.c_double
-    lib.oracle_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, D, P, I]
+    lib.oracle_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, D, P, I, P]
     lib.oracle_prefill.restype = I
-    lib.oracle_prefill_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, D]
+    lib.oracle_prefill_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, P]
     lib.oracle_prefill_backward.restype = I
-    lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D]
+    lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, P]
     lib.oracle_decode.restype = I
-    lib.oracle_mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, D]
+    lib.oracle_mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, D, P]
     lib.oracle_mla_decode.restype = I
     lib.oracle_merge_partials.argtypes = [P, P, I, I, P, P]
     lib.oracle_merge_partials.restype = None
@@ -100,13 +100,23 @@ def max_threads() -> int:
     return int(_load().oracle_max_threads())
 
 
+def _sinks(sinks, hq):
+    if sinks is None:
+        return None, None
+    a = _f32(sinks).reshape(-1)
+    assert a.shape == (hq,)
+    return a, _ptr(a)
+
+
 def prefill(q, k, v, *, causal: bool, window: int = 0, scale: float,
-            rows=None):
+            rows=None, sinks=None):
     """Exact attention forward.
 
     q:[B,hq,T,d]  k,v:[B,hkv,T,d].  ``rows`` optionally lists the query
-    positions to evaluate (all T when None).  Returns (o, lse):
-    o:[B,hq,n_rows,d] float64, lse:[B,hq,n_rows] float64 (natural log).
+    positions to evaluate (all T when None); ``sinks`` optionally gives one
+    sink logit per query head (an extra softmax-denominator term, in the
+    units of the scaled scores).  Returns (o, lse): o:[B,hq,n_rows,d]
+    float64, lse:[B,hq,n_rows] float64 (natural log).
     """
     q, k, v = _f32(q), _f32(k), _f32(v)
     B, hq, T, d = q.shape
@@ -121,15 +131,17 @@ def prefill(q, k, v, *, causal: bool, window: int = 0, scale: float,
         n_rows, rows_ptr = int(rows_arr.size), _ptr(rows_arr)
     o = np.zeros((B, hq, n_rows, d), dtype=np.float64)
     lse = np.zeros((B, hq, n_rows), dtype=np.float64)
+    sk, sk_ptr = _sinks(sinks, hq)
     rc = _load().oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                 B, T, hq, hkv, d, int(bool(causal)),
-                                int(window), float(scale), rows_ptr, n_rows)
+                                int(window), float(scale), rows_ptr, n_rows, sk_ptr)
     if rc != 0:
         raise ValueError("oracle_prefill: invalid shape")
     return o, lse
 
 
-def prefill_backward(q, k, v, dout, *, causal: bool, window: int = 0, scale: float):
+def prefill_backward(q, k, v, dout, *, causal: bool, window: int = 0, scale: float,
+                     sinks=None):
     """Gradients of the exact attention forward with respect to q, k, v for
     the output gradient ``dout``.  q, dout:[B,hq,T,d]  k,v:[B,hkv,T,d].
     Returns (dq, dk, dv) float64, shaped like q, k, v; dk and dv sum over the
@@ -141,15 +153,16 @@ def prefill_backward(q, k, v, dout, *, causal: bool, window: int = 0, scale: flo
     dq = np.zeros((B, hq, T, d), dtype=np.float64)
     dk = np.zeros((B, hkv, T, d), dtype=np.float64)
     dv = np.zeros((B, hkv, T, d), dtype=np.float64)
+    sk, sk_ptr = _sinks(sinks, hq)
     rc = _load().oracle_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                          _ptr(dq), _ptr(dk), _ptr(dv), B, T, hq, hkv, d,
-                                         int(bool(causal)), int(window), float(scale))
+                                         int(bool(causal)), int(window), float(scale), sk_ptr)
     if rc != 0:
         raise ValueError("oracle_prefill_backward: invalid shape")
     return dq, dk, dv
 
 
-def decode(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale: float):
+def decode(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale: float, sinks=None):
     """Single-token decode.  q:[B,hq,d] (or [B,hq,1,d]),
     caches:[B,hkv,S_max,d], seq_lens:[B].  Returns (o:[B,hq,d], lse:[B,hq])."""
     q = _f32(q)
@@ -163,15 +176,16 @@ def decode(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale: float):
     assert lens.shape == (B,)
     o = np.zeros((B, hq, d), dtype=np.float64)
     lse = np.zeros((B, hq), dtype=np.float64)
+    sk, sk_ptr = _sinks(sinks, hq)
     rc = _load().oracle_decode(_ptr(q), _ptr(kc), _ptr(vc), _ptr(lens),
                                _ptr(o), _ptr(lse), B, S_max, hq, hkv, d,
-                               int(window), float(scale))
+                               int(window), float(scale), sk_ptr)
     if rc != 0:
         raise ValueError("oracle_decode: invalid shape")
     return o, lse
 
 
-def mla_decode(q, cache, seq_lens, *, d_c: int, d_r: int, scale: float):
+def mla_decode(q, cache, seq_lens, *, d_c: int, d_r: int, scale: float, sinks=None):
     """MLA absorbed decode.  q:[B,H,d_c+d_r]  cache:[B,S_max,d_c+d_r].
     Returns (o:[B,H,d_c], lse:[B,H])."""
     q, c = _f32(q), _f32(cache)
@@ -182,9 +196,10 @@ def mla_decode(q, cache, seq_lens, *, d_c: int, d_r: int, scale: float):
     assert lens.shape == (B,)
     o = np.zeros((B, H, d_c), dtype=np.float64)
     lse = np.zeros((B, H), dtype=np.float64)
+    sk, sk_ptr = _sinks(sinks, H)
     rc = _load().oracle_mla_decode(_ptr(q), _ptr(c), _ptr(lens), _ptr(o),
                                    _ptr(lse), B, S_max, H, d_c, d_r,
-                                   float(scale))
+                                   float(scale), sk_ptr)
     if rc != 0:
         raise ValueError("oracle_mla_decode: invalid shape")
     return o, lse

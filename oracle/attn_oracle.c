@@ -60,18 +60,22 @@ static int prefill_visible(long i, long j, int causal, int window)
 
 /* softmax over the visible entries of s[0..n), then out[d] = sum_j p_j v_j[d].
  * v_row(j) points at the value row of key j (stride vstride floats).
+ * `sink` (-INFINITY for none) is an extra logit in the softmax denominator
+ * with no value row ("Attention Engineering ...", section 5, failure mode
+ * 2: a learnable scalar sink logit in the denominator).
  * Writes out[0..dv) and *lse. */
 static void softmax_mix(const double *s, const unsigned char *vis, long n,
                         const float *v, long vstride, int dv,
-                        double *out, double *lse, double *p)
+                        double *out, double *lse, double *p, double sink)
 {
     double m = -INFINITY;
     long any = 0;
     for (long j = 0; j < n; ++j)
         if (vis[j]) { if (!any || s[j] > m) m = s[j]; any = 1; }
     for (int d = 0; d < dv; ++d) out[d] = 0.0;
-    if (!any) { *lse = -INFINITY; return; }
-    double l = 0.0;
+    if (sink != -INFINITY && (!any || sink > m)) m = sink;
+    if (!any) { *lse = sink; return; }
+    double l = sink != -INFINITY ? exp(sink - m) : 0.0;
     for (long j = 0; j < n; ++j) {
         p[j] = vis[j] ? exp(s[j] - m) : 0.0;
         l += p[j];
@@ -96,7 +100,7 @@ int oracle_prefill(const float *q, const float *k, const float *v,
                    double *o, double *lse,
                    int B, int T, int hq, int hkv, int d,
                    int causal, int window, double scale,
-                   const int *rows, int n_rows)
+                   const int *rows, int n_rows, const float *sinks)
 {
     if (B < 0 || T < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv) return -1;
     if (!rows) n_rows = T;
@@ -126,7 +130,8 @@ int oracle_prefill(const float *q, const float *k, const float *v,
                 vis[j] = (unsigned char)prefill_visible(i, j, causal, window);
             }
             double l_out;
-            softmax_mix(s, vis, T, vb, d, d, o + u * d, &l_out, p);
+            softmax_mix(s, vis, T, vb, d, d, o + u * d, &l_out, p,
+                        sinks ? (double)sinks[h] : -INFINITY);
             if (lse) lse[u] = l_out;
         }
         free(s); free(p); free(vis);
@@ -151,7 +156,10 @@ int oracle_prefill(const float *q, const float *k, const float *v,
  *   dQ_i  = scale * sum_j dS_ij k_j
  *   dK_j  = scale * sum_i dS_ij q_i
  * where for K and V the sums over i also run over the query heads of the
- * group that shares them.
+ * group that shares them.  With a sink logit per query head (sinks may be
+ * NULL) P_ij is the weight under the sink-augmented denominator; the sink
+ * has no value row, so the formulas are otherwise unchanged (its own
+ * gradient is not computed here).
  *
  * Two plain passes: the first goes over query rows (log-sum-exp, the row
  * dot product sum_j P_ij dP_ij, and dQ_i); the second over keys of each
@@ -162,7 +170,7 @@ int oracle_prefill(const float *q, const float *k, const float *v,
 int oracle_prefill_backward(const float *q, const float *k, const float *v,
                             const float *dout, double *dq, double *dk, double *dv,
                             int B, int T, int hq, int hkv, int d,
-                            int causal, int window, double scale)
+                            int causal, int window, double scale, const float *sinks)
 {
     if (B < 0 || T < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv) return -1;
     const int G = hq / hkv;
@@ -206,7 +214,10 @@ int oracle_prefill_backward(const float *q, const float *k, const float *v,
             double *dqi = dq + u * d;
             for (int t = 0; t < d; ++t) dqi[t] = 0.0;
             if (!any) { lse[u] = -INFINITY; rdot[u] = 0.0; continue; }
-            double l = 0.0;
+            /* a sink logit only adds a term to the denominator (no value row) */
+            const double sk = sinks ? (double)sinks[h] : -INFINITY;
+            if (sk > m) m = sk;
+            double l = sk != -INFINITY ? exp(sk - m) : 0.0;
             for (long j = 0; j < T; ++j)
                 if (vis[j]) l += exp(s[j] - m);
             const double L = m + log(l);
@@ -270,7 +281,7 @@ int oracle_prefill_backward(const float *q, const float *k, const float *v,
 int oracle_decode(const float *q, const float *kc, const float *vc,
                   const int *seq_lens, double *o, double *lse,
                   int B, int S_max, int hq, int hkv, int d,
-                  int window, double scale)
+                  int window, double scale, const float *sinks)
 {
     if (B < 0 || S_max < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv) return -1;
     const int G = hq / hkv;
@@ -298,7 +309,8 @@ int oracle_decode(const float *q, const float *kc, const float *vc,
                 vis[j] = (unsigned char)(window <= 0 || i - j < window);
             }
             double l_out;
-            softmax_mix(s, vis, len, vb, d, d, o + u * d, &l_out, p);
+            softmax_mix(s, vis, len, vb, d, d, o + u * d, &l_out, p,
+                        sinks ? (double)sinks[h] : -INFINITY);
             if (lse) lse[u] = l_out;
         }
         free(s); free(p); free(vis);
@@ -318,7 +330,8 @@ int oracle_decode(const float *q, const float *kc, const float *vc,
  */
 int oracle_mla_decode(const float *q, const float *cache, const int *seq_lens,
                       double *o, double *lse,
-                      int B, int S_max, int H, int dc, int dr, double scale)
+                      int B, int S_max, int H, int dc, int dr, double scale,
+                      const float *sinks)
 {
     if (B < 0 || S_max < 0 || H <= 0 || dc <= 0 || dr < 0) return -1;
     const int dk = dc + dr;
@@ -345,7 +358,8 @@ int oracle_mla_decode(const float *q, const float *cache, const int *seq_lens,
                 vis[j] = 1;
             }
             double l_out;
-            softmax_mix(s, vis, len, cb, dk, dc, o + u * dc, &l_out, p);
+            softmax_mix(s, vis, len, cb, dk, dc, o + u * dc, &l_out, p,
+                        sinks ? (double)sinks[u % H] : -INFINITY);
             if (lse) lse[u] = l_out;
         }
         free(s); free(p); free(vis);
