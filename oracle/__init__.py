@@ -65,7 +65,7 @@ def _load():
     D = ctypes.c_double
     lib.oracle_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, D, P, I, P]
     lib.oracle_prefill.restype = I
-    lib.oracle_prefill_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, P]
+    lib.oracle_prefill_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, P, P]
     lib.oracle_prefill_backward.restype = I
     lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, P]
     lib.oracle_decode.restype = I
@@ -141,11 +141,12 @@ def prefill(q, k, v, *, causal: bool, window: int = 0, scale: float,
 
 
 def prefill_backward(q, k, v, dout, *, causal: bool, window: int = 0, scale: float,
-                     sinks=None):
+                     sinks=None, return_dsinks: bool = False):
     """Gradients of the exact attention forward with respect to q, k, v for
     the output gradient ``dout``.  q, dout:[B,hq,T,d]  k,v:[B,hkv,T,d].
     Returns (dq, dk, dv) float64, shaped like q, k, v; dk and dv sum over the
-    query heads of each K/V group."""
+    query heads of each K/V group.  With ``return_dsinks`` (needs ``sinks``)
+    the gradient of the sink logits, [hq] float64, is appended."""
     q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
     B, hq, T, d = q.shape
     hkv = k.shape[1]
@@ -154,12 +155,15 @@ def prefill_backward(q, k, v, dout, *, causal: bool, window: int = 0, scale: flo
     dk = np.zeros((B, hkv, T, d), dtype=np.float64)
     dv = np.zeros((B, hkv, T, d), dtype=np.float64)
     sk, sk_ptr = _sinks(sinks, hq)
+    assert sinks is not None or not return_dsinks
+    ds = np.zeros(hq, dtype=np.float64)
     rc = _load().oracle_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                          _ptr(dq), _ptr(dk), _ptr(dv), B, T, hq, hkv, d,
-                                         int(bool(causal)), int(window), float(scale), sk_ptr)
+                                         int(bool(causal)), int(window), float(scale), sk_ptr,
+                                         _ptr(ds) if return_dsinks else None)
     if rc != 0:
         raise ValueError("oracle_prefill_backward: invalid shape")
-    return dq, dk, dv
+    return (dq, dk, dv, ds) if return_dsinks else (dq, dk, dv)
 
 
 def decode(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale: float, sinks=None):

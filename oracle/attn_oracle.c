@@ -158,8 +158,10 @@ int oracle_prefill(const float *q, const float *k, const float *v,
  * where for K and V the sums over i also run over the query heads of the
  * group that shares them.  With a sink logit per query head (sinks may be
  * NULL) P_ij is the weight under the sink-augmented denominator; the sink
- * has no value row, so the formulas are otherwise unchanged (its own
- * gradient is not computed here).
+ * has no value row, so the formulas are otherwise unchanged.  The sink's
+ * own gradient (dsinks may be NULL) is the derivative of the loss through
+ * the denominator alone: with P_i = exp(sink - lse_i) the sink's weight in
+ * row i, dsink = -sum over the head's rows of P_i sum_j P_ij dP_ij.
  *
  * Two plain passes: the first goes over query rows (log-sum-exp, the row
  * dot product sum_j P_ij dP_ij, and dQ_i); the second over keys of each
@@ -170,14 +172,16 @@ int oracle_prefill(const float *q, const float *k, const float *v,
 int oracle_prefill_backward(const float *q, const float *k, const float *v,
                             const float *dout, double *dq, double *dk, double *dv,
                             int B, int T, int hq, int hkv, int d,
-                            int causal, int window, double scale, const float *sinks)
+                            int causal, int window, double scale, const float *sinks,
+                            double *dsinks)
 {
     if (B < 0 || T < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv) return -1;
     const int G = hq / hkv;
     const long rows = (long)B * hq * T;
     double *lse = (double *)malloc(sizeof(double) * (rows > 0 ? rows : 1));
     double *rdot = (double *)malloc(sizeof(double) * (rows > 0 ? rows : 1));
-    if (!lse || !rdot) { free(lse); free(rdot); return -1; }
+    double *sgrad = (double *)malloc(sizeof(double) * (rows > 0 ? rows : 1));
+    if (!lse || !rdot || !sgrad) { free(lse); free(rdot); free(sgrad); return -1; }
     /* pass 1: one query row at a time */
 #pragma omp parallel
     {
@@ -213,7 +217,7 @@ int oracle_prefill_backward(const float *q, const float *k, const float *v,
             }
             double *dqi = dq + u * d;
             for (int t = 0; t < d; ++t) dqi[t] = 0.0;
-            if (!any) { lse[u] = -INFINITY; rdot[u] = 0.0; continue; }
+            if (!any) { lse[u] = -INFINITY; rdot[u] = 0.0; sgrad[u] = 0.0; continue; }
             /* a sink logit only adds a term to the denominator (no value row) */
             const double sk = sinks ? (double)sinks[h] : -INFINITY;
             if (sk > m) m = sk;
@@ -226,6 +230,7 @@ int oracle_prefill_backward(const float *q, const float *k, const float *v,
                 if (vis[j]) rd += exp(s[j] - L) * dp[j];
             lse[u] = L;
             rdot[u] = rd;
+            sgrad[u] = sk != -INFINITY ? -exp(sk - L) * rd : 0.0;
             for (long j = 0; j < T; ++j) {
                 if (!vis[j]) continue;
                 const double ds = exp(s[j] - L) * (dp[j] - rd);
@@ -234,6 +239,13 @@ int oracle_prefill_backward(const float *q, const float *k, const float *v,
         }
         free(s); free(dp); free(vis);
     }
+    if (dsinks)
+        for (long h = 0; h < hq; ++h) {
+            double acc = 0.0;
+            for (long b = 0; b < B; ++b)
+                for (long i = 0; i < T; ++i) acc += sgrad[(b * hq + h) * (long)T + i];
+            dsinks[h] = acc;
+        }
     /* pass 2: one key of one K/V head at a time, over the group's query rows */
     const long keys = (long)B * hkv * T;
 #pragma omp parallel for schedule(dynamic, 16)
@@ -266,7 +278,7 @@ int oracle_prefill_backward(const float *q, const float *k, const float *v,
             }
         }
     }
-    free(lse); free(rdot);
+    free(lse); free(rdot); free(sgrad);
     return 0;
 }
 

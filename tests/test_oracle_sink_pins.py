@@ -6,8 +6,9 @@ section 5, failure mode 2).  So, against the same row without a sink:
   O_sink = O / (1 + exp(s - L)),  L_sink = logaddexp(L, s),
 a closed form in the no-sink oracle's outputs; a very negative sink changes
 nothing; a row with no visible key gets O = 0 and L = s.  The gradients
-with a sink (the sink's own excepted) are pinned by torch autograd through
-an fp64 softmax that carries the extra column."""
+with a sink, the sink's own included, are pinned by torch autograd through
+an fp64 softmax that carries the extra column, and the sink's gradient also
+by central differences of the (closed-form pinned) forward."""
 import numpy as np
 import pytest
 import torch
@@ -78,15 +79,43 @@ def test_backward_with_sink_matches_autograd(oracle_mod):
     sinks = np.array([0.3, -1.0, 2.0, 0.0], dtype=np.float32)
     scale = 0.35
     qt, kt, vt = (torch.from_numpy(x.astype(np.float64)).requires_grad_(True) for x in (q, k, v))
+    st = torch.from_numpy(sinks.astype(np.float64)).requires_grad_(True)
     kr = kt.repeat_interleave(G, dim=1)
     vr = vt.repeat_interleave(G, dim=1)
     s = scale * qt @ kr.transpose(-1, -2)
     mask = torch.tril(torch.ones(T, T, dtype=torch.bool))
     s = s.masked_fill(~mask, float("-inf"))
-    sk = torch.from_numpy(sinks.astype(np.float64)).view(1, hq, 1, 1).expand(B, hq, T, 1)
+    sk = st.view(1, hq, 1, 1).expand(B, hq, T, 1)
     w = torch.softmax(torch.cat([s, sk], dim=-1), dim=-1)[..., :T]
     out = w @ vr
     out.backward(torch.from_numpy(do.astype(np.float64)))
-    dq, dk, dv = oracle_mod.prefill_backward(q, k, v, do, causal=True, scale=scale, sinks=sinks)
-    for name, a, b in (("dq", dq, qt.grad), ("dk", dk, kt.grad), ("dv", dv, vt.grad)):
+    dq, dk, dv, ds = oracle_mod.prefill_backward(q, k, v, do, causal=True, scale=scale,
+                                                 sinks=sinks, return_dsinks=True)
+    for name, a, b in (("dq", dq, qt.grad), ("dk", dk, kt.grad), ("dv", dv, vt.grad),
+                       ("dsinks", ds, st.grad)):
         assert np.abs(a - b.numpy()).max() < 1e-10, name
+
+
+def test_sink_gradient_matches_finite_differences(oracle_mod):
+    """d loss / d sink_h by central differences of the oracle's own forward
+    (loss = sum o * dout) -- the forward is pinned by the closed form above,
+    the gradient is a separate code path."""
+    rng = _rng(131)
+    B, T, hq, hkv, d = 2, 11, 3, 1, 4
+    q = rng.standard_normal((B, hq, T, d)).astype(np.float32)
+    k = rng.standard_normal((B, hkv, T, d)).astype(np.float32)
+    v = rng.standard_normal((B, hkv, T, d)).astype(np.float32)
+    do = rng.standard_normal((B, hq, T, d)).astype(np.float32)
+    sinks = np.array([0.5, -0.25, 1.5], dtype=np.float32)
+    scale = 0.4
+    *_, ds = oracle_mod.prefill_backward(q, k, v, do, causal=True, window=5, scale=scale,
+                                         sinks=sinks, return_dsinks=True)
+    eps = 2.0 ** -10
+    for h in range(hq):
+        sp, sm = sinks.copy(), sinks.copy()
+        sp[h] += eps
+        sm[h] -= eps
+        op, _ = oracle_mod.prefill(q, k, v, causal=True, window=5, scale=scale, sinks=sp)
+        om, _ = oracle_mod.prefill(q, k, v, causal=True, window=5, scale=scale, sinks=sm)
+        num = (np.sum(op * do) - np.sum(om * do)) / (2 * eps)
+        assert abs(num - ds[h]) < 1e-6, h
