@@ -32,7 +32,8 @@
  *    outputs are rounded to bf16 (round-to-nearest-even).
  *  - `lse`, where offered, receives the natural-log log-sum-exp of the
  *    scaled, masked score row, L = m + ln(l); it may be NULL.  A row with no
- *    visible key gets O = 0 and L = -inf.
+ *    visible key gets O = 0 and L = -inf (the sink logit, where one is
+ *    given: see attn_prefill).
  *  - Inputs are checked on the host before anything is launched.  Failures
  *    return a status and enqueue nothing.  ATTN_ERR_HIP reports a launch
  *    error from the HIP runtime (hipGetLastError after the launch).
@@ -77,13 +78,23 @@ typedef enum {
  * window > 0 requires causal != 0.  causal == 0 with window == 0 is full
  * (bidirectional) attention.
  *
+ * sinks: NULL, or [h_q] float32 in device memory, one sink logit per query
+ * head: an extra term exp(sinks[h]) in every row's softmax denominator that
+ * carries no value row, so a row may put weight on "nothing" ("Attention
+ * Engineering ...", section 5, failure mode 2: a learnable scalar logit in
+ * the denominator).  It is in the units of the scaled scores (natural log):
+ *   o_i = sum_j exp(s_ij) v_j / (exp(sinks[h]) + sum_j exp(s_ij)),
+ *   lse_i = log(exp(sinks[h]) + sum_j exp(s_ij)).
+ * A row with no visible key gets o = 0 and lse = sinks[h] (-inf without a
+ * sink).  Every entry point below that takes `sinks` reads it the same way.
+ *
  * Supported: dtype ATTN_BF16 with d_h = 128 (MFMA kernel); dtype ATTN_F32
  * with d_h in {16, 32, 64, 128}.  Any B >= 1, T >= 1, h_q a multiple of h_kv.
  */
 attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
                            float *lse, int B, int T, int h_q, int h_kv, int d_h,
                            attn_dtype_t dtype, int causal, int window, float scale,
-                           hipStream_t stream);
+                           const float *sinks, hipStream_t stream);
 
 /*
  * attn_prefill_backward -- gradients of attn_prefill with respect to q, k, v.
@@ -107,6 +118,14 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
  * MFMA operands and the outputs to bf16 (round-to-nearest-even).  No atomics:
  * the result is bitwise reproducible.
  *
+ * sinks, dsinks: for a forward run with sink logits, o and lse already
+ * include the sink's denominator term, so the formulas above hold as they
+ * stand (the sink has no value row).  When dsinks ([h_q] float32, device) is
+ * not NULL, the sinks' gradient is written there:
+ *   dsinks[h] = -sum over b, i of exp(sinks[h] - lse_i) D_i,
+ * summed in a fixed order.  dsinks without sinks is ATTN_ERR_INVALID_ARG;
+ * sinks alone is read for nothing.
+ *
  * workspace: caller device memory of at least
  * attn_prefill_backward_workspace_size(B, T, h_q) bytes (per-row lse in log2
  * units and D, rows padded to a multiple of 64); it is overwritten.
@@ -119,6 +138,7 @@ attn_status_t attn_prefill_backward(const void *q, const void *k, const void *v,
                                     void *dq, void *dk, void *dv,
                                     int B, int T, int h_q, int h_kv, int d_h,
                                     attn_dtype_t dtype, int causal, int window, float scale,
+                                    const float *sinks, float *dsinks,
                                     void *workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
@@ -142,6 +162,8 @@ attn_status_t attn_prefill_backward(const void *q, const void *k, const void *v,
  * positions (0 = the library's choice; otherwise a positive multiple of
  * 64), each chunk is attended to independently and the partial results are
  * merged with their log-sum-exp weights; the split changes only rounding.
+ * sinks: NULL or [h_q] sink logits, as for attn_prefill (a sequence with
+ * seq_lens[b] = 0 gets o = 0 and lse = sinks[h]).
  * Supported: d_h = 128, any h_q that is a multiple of h_kv.
  */
 size_t attn_decode_workspace_size(int B, int S_max, int h_q, int h_kv, int d_h,
@@ -149,7 +171,7 @@ size_t attn_decode_workspace_size(int B, int S_max, int h_q, int h_kv, int d_h,
 attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache,
                           void *o, float *lse, const int32_t *seq_lens,
                           int B, int S_max, int h_q, int h_kv, int d_h,
-                          int window, float scale, int split_tokens,
+                          int window, float scale, const float *sinks, int split_tokens,
                           void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
@@ -168,15 +190,15 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
  *   seq_lens : [B] int32, device memory, clamped to [0, S_max].
  *
  * score_j = scale * (q[:d_c] . c_j + q[d_c:] . kR_j); the value of token j
- * is the first d_c entries of the same cache row.  split_tokens as for
- * attn_decode.  Supported: d_c = 512, d_r = 64, h_q a multiple of 16.
+ * is the first d_c entries of the same cache row.  split_tokens and sinks
+ * as for attn_decode.  Supported: d_c = 512, d_r = 64, h_q a multiple of 16.
  */
 size_t mla_decode_workspace_size(int B, int S_max, int h_q, int d_c, int d_r,
                                  int split_tokens);
 attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *lse,
                          const int32_t *seq_lens, int B, int S_max, int h_q,
-                         int d_c, int d_r, float scale, int split_tokens,
-                         void *workspace, size_t workspace_bytes,
+                         int d_c, int d_r, float scale, const float *sinks,
+                         int split_tokens, void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
 /*
@@ -199,7 +221,7 @@ attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *ls
  *                      wrong data).
  *   seq_lens         : as for the contiguous calls, clamped to
  *                      [0, max_blocks * page_size].
- * Everything else (q, o, lse, window, scale, split_tokens, workspace,
+ * Everything else (q, o, lse, window, scale, sinks, split_tokens, workspace,
  * errors) is as in attn_decode / mla_decode with S_max = max_blocks *
  * page_size; the *_paged_workspace_size functions return exactly that.
  * page_size must be a positive multiple of 32 (ATTN_ERR_UNSUPPORTED
@@ -212,23 +234,23 @@ attn_status_t attn_decode_paged(const void *q, const void *k_pages, const void *
                                 void *o, float *lse, const int32_t *seq_lens,
                                 const int32_t *block_table, int B, int max_blocks,
                                 int page_size, int num_pages, int h_q, int h_kv, int d_h,
-                                int window, float scale, int split_tokens,
-                                void *workspace, size_t workspace_bytes,
+                                int window, float scale, const float *sinks,
+                                int split_tokens, void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 size_t mla_decode_paged_workspace_size(int B, int max_blocks, int page_size, int h_q,
                                        int d_c, int d_r, int split_tokens);
 attn_status_t mla_decode_paged(const void *q, const void *kv_pages, void *o, float *lse,
                                const int32_t *seq_lens, const int32_t *block_table,
                                int B, int max_blocks, int page_size, int num_pages,
-                               int h_q, int d_c, int d_r, float scale, int split_tokens,
-                               void *workspace, size_t workspace_bytes,
+                               int h_q, int d_c, int d_r, float scale, const float *sinks,
+                               int split_tokens, void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *attn_status_string(attn_status_t status);
 
 /* ABI version of this header (bumped on incompatible change). */
-#define MI355ATTN_ABI_VERSION 1
+#define MI355ATTN_ABI_VERSION 2
 int attn_abi_version(void);
 
 #ifdef __cplusplus

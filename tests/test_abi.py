@@ -48,7 +48,7 @@ def test_status_strings(lib):
     assert ta.status_string(0) == "ok"
     for s in range(1, 5):
         assert ta.status_string(s) not in ("ok", "unknown status")
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
@@ -59,7 +59,8 @@ def _prefill(lib, **kw):
              dtype=1, causal=1, window=0, scale=0.1)
     a.update(kw)
     return lib.attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["T"], a["hq"],
-                            a["hkv"], a["d"], a["dtype"], a["causal"], a["window"], a["scale"], None)
+                            a["hkv"], a["d"], a["dtype"], a["causal"], a["window"], a["scale"], None,
+                            None)
 
 
 def test_prefill_validation(lib):
@@ -83,13 +84,15 @@ def test_prefill_backward_validation(lib):
     def bwd(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
                  B=1, T=100, hq=4, hkv=2, d=128, dtype=1, causal=1, window=0, scale=0.1,
-                 ws=FAKE, wsb=1 << 30)
+                 sinks=None, dsinks=None, ws=FAKE, wsb=1 << 30)
         a.update(kw)
         return lib.attn_prefill_backward(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
                                          a["dq"], a["dk"], a["dv"], a["B"], a["T"], a["hq"],
                                          a["hkv"], a["d"], a["dtype"], a["causal"], a["window"],
-                                         a["scale"], a["ws"], a["wsb"], None)
+                                         a["scale"], a["sinks"], a["dsinks"], a["ws"], a["wsb"],
+                                         None)
     assert bwd(lse=None) == 1
+    assert bwd(dsinks=FAKE) == 1                    # a sink gradient needs the sinks
     assert bwd(dk=None) == 1
     assert bwd(T=0) == 1
     assert bwd(hq=6, hkv=4) == 1
@@ -110,7 +113,7 @@ def test_decode_validation(lib):
                  window=0, scale=0.1, split=0, ws=FAKE, wsb=1 << 30)
         a.update(kw)
         return lib.attn_decode(a["q"], a["k"], a["v"], a["o"], None, a["lens"], a["B"], a["S"],
-                               a["hq"], a["hkv"], a["d"], a["window"], a["scale"], a["split"],
+                               a["hq"], a["hkv"], a["d"], a["window"], a["scale"], None, a["split"],
                                a["ws"], a["wsb"], None)
     assert dec(lens=None) == 1
     assert dec(hq=7) == 1
@@ -131,7 +134,8 @@ def test_paged_validation(lib):
         a.update(kw)
         return lib.attn_decode_paged(a["q"], a["k"], a["v"], a["o"], None, a["lens"], a["bt"],
                                      a["B"], a["mb"], a["ps"], a["np_"], a["hq"], a["hkv"], a["d"],
-                                     a["window"], a["scale"], a["split"], a["ws"], a["wsb"], None)
+                                     a["window"], a["scale"], None, a["split"], a["ws"], a["wsb"],
+                                     None)
     assert dec(bt=None) == 1
     assert dec(mb=0) == 1
     assert dec(np_=0) == 1
@@ -150,7 +154,7 @@ def test_paged_validation(lib):
         a.update(kw)
         return lib.mla_decode_paged(a["q"], a["c"], a["o"], None, a["lens"], a["bt"], a["B"],
                                     a["mb"], a["ps"], a["np_"], a["H"], a["dc"], a["dr"],
-                                    a["scale"], a["split"], a["ws"], a["wsb"], None)
+                                    a["scale"], None, a["split"], a["ws"], a["wsb"], None)
     assert mla(bt=None) == 1
     assert mla(ps=100) == 2
     assert mla(dc=256) == 2
@@ -166,7 +170,8 @@ def test_mla_validation(lib):
                  split=0, ws=FAKE, wsb=1 << 30)
         a.update(kw)
         return lib.mla_decode(a["q"], a["c"], a["o"], None, a["lens"], a["B"], a["S"], a["H"],
-                              a["dc"], a["dr"], a["scale"], a["split"], a["ws"], a["wsb"], None)
+                              a["dc"], a["dr"], a["scale"], None, a["split"], a["ws"], a["wsb"],
+                              None)
     assert mla(c=None) == 1
     assert mla(scale=float("nan")) == 1
     assert mla(scale=0.0) == 1

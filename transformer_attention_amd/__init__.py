@@ -68,28 +68,29 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             f"{path} is missing: build it with `python -m transformer_attention_amd.build`")
     lib = ctypes.CDLL(path)
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    lib.attn_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+    lib.attn_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, P]
     lib.attn_prefill.restype = I
     lib.attn_prefill_backward_workspace_size.argtypes = [I, I, I]
     lib.attn_prefill_backward_workspace_size.restype = Z
     lib.attn_prefill_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F,
-                                          P, Z, P]
+                                          P, P, P, Z, P]
     lib.attn_prefill_backward.restype = I
     lib.attn_decode_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.attn_decode_workspace_size.restype = Z
-    lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, P, I, P, Z, P]
     lib.attn_decode.restype = I
     lib.mla_decode_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.mla_decode_workspace_size.restype = Z
-    lib.mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, Z, P]
+    lib.mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P, I, P, Z, P]
     lib.mla_decode.restype = I
     lib.attn_decode_paged_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.attn_decode_paged_workspace_size.restype = Z
-    lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, I, P, Z,
+                                      P]
     lib.attn_decode_paged.restype = I
     lib.mla_decode_paged_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.mla_decode_paged_workspace_size.restype = Z
-    lib.mla_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.mla_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, I, P, Z, P]
     lib.mla_decode_paged.restype = I
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -134,10 +135,21 @@ def _require(t, name, dtype, device=None, ndim=None):
 _DT = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
 
 
+def _sinks(sinks, h_q, device):
+    """Optional sink logits: one fp32 value per query head on the device."""
+    if sinks is None:
+        return None
+    _require(sinks, "sinks", torch.float32, device)
+    if sinks.numel() != h_q:
+        raise ValueError(f"sinks must hold h_q = {h_q} values")
+    return sinks
+
+
 def attn_prefill(q, k, v, *, causal: bool = True, window: int = 0, scale=None,
-                 o=None, lse=None, return_lse: bool = False):
+                 sinks=None, o=None, lse=None, return_lse: bool = False):
     """q:[B,h_q,T,d]  k,v:[B,h_kv,T,d] (bf16 or fp32, contiguous, same device).
-    Returns o (and lse:[B,h_q,T] fp32 when requested)."""
+    sinks: optional fp32[h_q] sink logits.  Returns o (and lse:[B,h_q,T] fp32
+    when requested)."""
     lib = load_library()
     if q.dtype not in _DT:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -161,9 +173,10 @@ def attn_prefill(q, k, v, *, causal: bool = True, window: int = 0, scale=None,
         _require(lse, "lse", torch.float32, q.device)
         if lse.numel() != B * hq * T:
             raise ValueError("lse shape mismatch")
+    sinks = _sinks(sinks, hq, q.device)
     st = lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, hq,
                           hkv, d, _DT[q.dtype], int(bool(causal)), int(window),
-                          float(scale), _stream(q.device))
+                          float(scale), _ptr(sinks), _stream(q.device))
     _check(st, "attn_prefill")
     return (o, lse) if (return_lse or lse is not None) else o
 
@@ -173,9 +186,12 @@ def attn_prefill_backward_workspace_size(B, T, h_q) -> int:
 
 
 def attn_prefill_backward(q, k, v, o, dout, lse, *, causal: bool = True, window: int = 0,
-                          scale=None, dq=None, dk=None, dv=None, workspace=None):
+                          scale=None, sinks=None, return_dsinks: bool = False, dq=None,
+                          dk=None, dv=None, dsinks=None, workspace=None):
     """Gradients of attn_prefill.  q, o, dout:[B,h_q,T,128] bf16; k,v:[B,h_kv,T,128]
-    bf16; lse:[B,h_q,T] fp32 (the forward's).  Returns (dq, dk, dv)."""
+    bf16; lse:[B,h_q,T] fp32 (the forward's).  Returns (dq, dk, dv), and the
+    sink logits' gradient fp32[h_q] as a fourth item with ``return_dsinks``
+    (which needs ``sinks``, the forward's)."""
     lib = load_library()
     _require(q, "q", torch.bfloat16, ndim=4)
     for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
@@ -203,12 +219,22 @@ def attn_prefill_backward(q, k, v, o, dout, lse, *, causal: bool = True, window:
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _require(workspace, "workspace", torch.uint8, q.device)
+    sinks = _sinks(sinks, hq, q.device)
+    if return_dsinks and sinks is None:
+        raise ValueError("return_dsinks needs sinks")
+    if return_dsinks and dsinks is None:
+        dsinks = torch.empty(hq, dtype=torch.float32, device=q.device)
+    if dsinks is not None:
+        _require(dsinks, "dsinks", torch.float32, q.device)
+        if dsinks.numel() != hq:
+            raise ValueError("dsinks shape mismatch")
     st = lib.attn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                    _ptr(dq), _ptr(dk), _ptr(dv), B, T, hq, hkv, d,
                                    _DT[q.dtype], int(bool(causal)), int(window), float(scale),
-                                   _ptr(workspace), workspace.numel(), _stream(q.device))
+                                   _ptr(sinks), _ptr(dsinks), _ptr(workspace),
+                                   workspace.numel(), _stream(q.device))
     _check(st, "attn_prefill_backward")
-    return dq, dk, dv
+    return (dq, dk, dv, dsinks) if (return_dsinks or dsinks is not None) else (dq, dk, dv)
 
 
 def attn_decode_workspace_size(B, S_max, h_q, h_kv, d_h, split_tokens=0) -> int:
@@ -217,7 +243,7 @@ def attn_decode_workspace_size(B, S_max, h_q, h_kv, d_h, split_tokens=0) -> int:
 
 
 def attn_decode(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale=None,
-                split_tokens: int = 0, o=None, lse=None, workspace=None,
+                sinks=None, split_tokens: int = 0, o=None, lse=None, workspace=None,
                 return_lse: bool = False):
     """q:[B,h_q,d] or [B,h_q,1,d] bf16; caches:[B,h_kv,S_max,d] bf16;
     seq_lens: int32[B] on the device.  Returns o shaped like q."""
@@ -250,9 +276,10 @@ def attn_decode(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale=None,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _require(workspace, "workspace", None, q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
+    sinks = _sinks(sinks, hq, q.device)
     st = lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
                          _ptr(seq_lens), B, S_max, hq, hkv, d, int(window),
-                         float(scale), int(split_tokens), _ptr(workspace), ws_bytes,
+                         float(scale), _ptr(sinks), int(split_tokens), _ptr(workspace), ws_bytes,
                          _stream(q.device))
     _check(st, "attn_decode")
     return (o, lse) if (return_lse or lse is not None) else o
@@ -264,7 +291,7 @@ def mla_decode_workspace_size(B, S_max, h_q, d_c=512, d_r=64, split_tokens=0) ->
 
 
 def mla_decode(q, kv_cache, seq_lens, *, d_c: int = 512, d_r: int = 64, scale: float,
-               split_tokens: int = 0, o=None, lse=None, workspace=None,
+               sinks=None, split_tokens: int = 0, o=None, lse=None, workspace=None,
                return_lse: bool = False):
     """q:[B,H,d_c+d_r] bf16; kv_cache:[B,S_max,d_c+d_r] bf16; seq_lens int32[B].
     Returns o:[B,H,d_c] bf16 (the latent context before W_UV)."""
@@ -290,15 +317,16 @@ def mla_decode(q, kv_cache, seq_lens, *, d_c: int = 512, d_r: int = 64, scale: f
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _require(workspace, "workspace", None, q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
+    sinks = _sinks(sinks, H, q.device)
     st = lib.mla_decode(_ptr(q), _ptr(kv_cache), _ptr(o), _ptr(lse), _ptr(seq_lens),
-                        B, S_max, H, d_c, d_r, float(scale), int(split_tokens),
+                        B, S_max, H, d_c, d_r, float(scale), _ptr(sinks), int(split_tokens),
                         _ptr(workspace), ws_bytes, _stream(q.device))
     _check(st, "mla_decode")
     return (o, lse) if (return_lse or lse is not None) else o
 
 
 def attn_decode_paged(q, k_pages, v_pages, seq_lens, block_table, *, window: int = 0, scale=None,
-                      split_tokens: int = 0, o=None, lse=None, workspace=None,
+                      sinks=None, split_tokens: int = 0, o=None, lse=None, workspace=None,
                       return_lse: bool = False):
     """q:[B,h_q,d] or [B,h_q,1,d] bf16; pages:[num_pages,h_kv,page_size,d] bf16;
     block_table: int32[B,max_blocks] and seq_lens: int32[B] on the device."""
@@ -337,14 +365,14 @@ def attn_decode_paged(q, k_pages, v_pages, seq_lens, block_table, *, window: int
     st = lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), _ptr(lse),
                                _ptr(seq_lens), _ptr(block_table), B, max_blocks, page_size,
                                num_pages, hq, hkv, d, int(window), float(scale),
-                               int(split_tokens), _ptr(workspace), ws_bytes, _stream(q.device))
+                               _ptr(_sinks(sinks, hq, q.device)), int(split_tokens), _ptr(workspace), ws_bytes, _stream(q.device))
     _check(st, "attn_decode_paged")
     return (o, lse) if (return_lse or lse is not None) else o
 
 
 def mla_decode_paged(q, kv_pages, seq_lens, block_table, *, d_c: int = 512, d_r: int = 64,
-                     scale: float, split_tokens: int = 0, o=None, lse=None, workspace=None,
-                     return_lse: bool = False):
+                     scale: float, sinks=None, split_tokens: int = 0, o=None, lse=None,
+                     workspace=None, return_lse: bool = False):
     """q:[B,H,d_c+d_r] bf16; kv_pages:[num_pages,page_size,d_c+d_r] bf16;
     block_table: int32[B,max_blocks] and seq_lens: int32[B] on the device."""
     lib = load_library()
@@ -374,7 +402,8 @@ def mla_decode_paged(q, kv_pages, seq_lens, block_table, *, d_c: int = 512, d_r:
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib.mla_decode_paged(_ptr(q), _ptr(kv_pages), _ptr(o), _ptr(lse), _ptr(seq_lens),
                               _ptr(block_table), B, max_blocks, page_size, num_pages, H, d_c,
-                              d_r, float(scale), int(split_tokens), _ptr(workspace), ws_bytes,
+                              d_r, float(scale), _ptr(_sinks(sinks, H, q.device)),
+                              int(split_tokens), _ptr(workspace), ws_bytes,
                               _stream(q.device))
     _check(st, "mla_decode_paged")
     return (o, lse) if (return_lse or lse is not None) else o

@@ -76,14 +76,15 @@ const char *attn_status_string(attn_status_t s) {
 
 attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse,
                            int B, int T, int h_q, int h_kv, int d_h, attn_dtype_t dtype,
-                           int causal, int window, float scale, hipStream_t stream) {
+                           int causal, int window, float scale, const float *sinks,
+                           hipStream_t stream) {
     if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(o)) return ATTN_ERR_INVALID_ARG;
     if (B <= 0 || T <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
     if (h_q % h_kv != 0) return ATTN_ERR_INVALID_ARG;
     if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_INVALID_ARG;
     if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_INVALID_ARG;
     if ((long long)B * h_q * T * d_h >= (1LL << 40)) return ATTN_ERR_UNSUPPORTED;
-    mi355::PrefillArgs a{q, k, v, o, lse, B, T, h_q, h_kv, d_h, causal ? 1 : 0, window, scale};
+    mi355::PrefillArgs a{q, k, v, o, lse, B, T, h_q, h_kv, d_h, causal ? 1 : 0, window, scale, sinks};
     hipError_t e;
     if (dtype == ATTN_BF16) {
         if (d_h != 128) return ATTN_ERR_UNSUPPORTED;
@@ -108,7 +109,8 @@ attn_status_t attn_prefill_backward(const void *q, const void *k, const void *v,
                                     const void *dout, const float *lse, void *dq, void *dk,
                                     void *dv, int B, int T, int h_q, int h_kv, int d_h,
                                     attn_dtype_t dtype, int causal, int window, float scale,
-                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                                    const float *sinks, float *dsinks, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
     if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(o) || bad_ptr(dout) || bad_ptr(lse) ||
         bad_ptr(dq) || bad_ptr(dk) || bad_ptr(dv))
         return ATTN_ERR_INVALID_ARG;
@@ -116,6 +118,7 @@ attn_status_t attn_prefill_backward(const void *q, const void *k, const void *v,
     if (h_q % h_kv != 0) return ATTN_ERR_INVALID_ARG;
     if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_INVALID_ARG;
     if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+    if (dsinks && !sinks) return ATTN_ERR_INVALID_ARG;
     if (dtype != ATTN_BF16 || d_h != 128) return ATTN_ERR_UNSUPPORTED;
     if ((long long)B * h_q * (T + 63) * d_h >= (1LL << 40)) return ATTN_ERR_UNSUPPORTED;
     if ((long long)B * h_q > 65535) return ATTN_ERR_UNSUPPORTED;
@@ -123,7 +126,8 @@ attn_status_t attn_prefill_backward(const void *q, const void *k, const void *v,
     if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     const int tpad = (T + 63) / 64 * 64;
     mi355::PrefillBwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, T, h_q, h_kv, d_h,
-                            causal ? 1 : 0, window, scale, static_cast<float *>(workspace), tpad};
+                            causal ? 1 : 0, window, scale, static_cast<float *>(workspace), tpad,
+                            sinks, dsinks};
     return mi355::launch_prefill_bwd_bf16_d128(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -142,8 +146,9 @@ size_t attn_decode_workspace_size(int B, int S_max, int h_q, int h_kv, int d_h, 
 
 attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *o,
                           float *lse, const int32_t *seq_lens, int B, int S_max, int h_q,
-                          int h_kv, int d_h, int window, float scale, int split_tokens,
-                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                          int h_kv, int d_h, int window, float scale, const float *sinks,
+                          int split_tokens, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
     if (bad_ptr(q) || bad_ptr(k_cache) || bad_ptr(v_cache) || bad_ptr(o) || bad_ptr(seq_lens))
         return ATTN_ERR_INVALID_ARG;
     if (B <= 0 || S_max <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
@@ -160,7 +165,8 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     float *ws_lse = reinterpret_cast<float *>(ws_end);
     int32_t *plan = reinterpret_cast<int32_t *>(ws_end + align_up((size_t)B * h_q * ns * sizeof(float), 256));
     mi355::DecodeArgs a{q, k_cache, v_cache, o, lse, seq_lens, B, S_max, h_q, h_kv, d_h,
-                        window, scale, split, ns, ws_o, ws_lse, plan, device_cu_count()};
+                        window, scale, split, ns, ws_o, ws_lse, plan, device_cu_count(),
+                        nullptr, 0, 0, 0, sinks};
     return mi355::launch_decode_bf16_d128(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -178,8 +184,9 @@ static bool bad_pages(const int32_t *block_table, int max_blocks, int page_size,
 attn_status_t attn_decode_paged(const void *q, const void *k_pages, const void *v_pages, void *o,
                                 float *lse, const int32_t *seq_lens, const int32_t *block_table,
                                 int B, int max_blocks, int page_size, int num_pages, int h_q,
-                                int h_kv, int d_h, int window, float scale, int split_tokens,
-                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                                int h_kv, int d_h, int window, float scale, const float *sinks,
+                                int split_tokens, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
     if (bad_ptr(q) || bad_ptr(k_pages) || bad_ptr(v_pages) || bad_ptr(o) || bad_ptr(seq_lens))
         return ATTN_ERR_INVALID_ARG;
     if (bad_pages(block_table, max_blocks, page_size, num_pages)) return ATTN_ERR_INVALID_ARG;
@@ -201,7 +208,7 @@ attn_status_t attn_decode_paged(const void *q, const void *k_pages, const void *
     int32_t *plan = reinterpret_cast<int32_t *>(ws_end + align_up((size_t)B * h_q * ns * sizeof(float), 256));
     mi355::DecodeArgs a{q, k_pages, v_pages, o, lse, seq_lens, B, S_max, h_q, h_kv, d_h,
                         window, scale, split, ns, ws_o, ws_lse, plan, device_cu_count(),
-                        block_table, max_blocks, page_size, num_pages};
+                        block_table, max_blocks, page_size, num_pages, sinks};
     return mi355::launch_decode_bf16_d128(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -215,8 +222,8 @@ size_t mla_decode_workspace_size(int B, int S_max, int h_q, int d_c, int d_r, in
 
 attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *lse,
                          const int32_t *seq_lens, int B, int S_max, int h_q, int d_c, int d_r,
-                         float scale, int split_tokens, void *workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+                         float scale, const float *sinks, int split_tokens, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
     if (bad_ptr(q) || bad_ptr(kv_cache) || bad_ptr(o) || bad_ptr(seq_lens)) return ATTN_ERR_INVALID_ARG;
     if (B <= 0 || S_max <= 0 || h_q <= 0 || d_c <= 0 || d_r < 0) return ATTN_ERR_INVALID_ARG;
     if (!isfinite(scale) || !(scale > 0.f) || split_tokens < 0 || split_tokens % 64)
@@ -231,7 +238,7 @@ attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *ls
     float *ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                               align_up((size_t)B * h_q * ns * d_c * sizeof(float), 256));
     mi355::MlaArgs a{q, kv_cache, o, lse, seq_lens, B, S_max, h_q, d_c, d_r, scale, split, ns,
-                     ws_o, ws_lse};
+                     ws_o, ws_lse, nullptr, 0, 0, 0, sinks};
     return mi355::launch_mla_decode_bf16(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -244,8 +251,8 @@ size_t mla_decode_paged_workspace_size(int B, int max_blocks, int page_size, int
 attn_status_t mla_decode_paged(const void *q, const void *kv_pages, void *o, float *lse,
                                const int32_t *seq_lens, const int32_t *block_table, int B,
                                int max_blocks, int page_size, int num_pages, int h_q, int d_c,
-                               int d_r, float scale, int split_tokens, void *workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
+                               int d_r, float scale, const float *sinks, int split_tokens,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (bad_ptr(q) || bad_ptr(kv_pages) || bad_ptr(o) || bad_ptr(seq_lens)) return ATTN_ERR_INVALID_ARG;
     if (bad_pages(block_table, max_blocks, page_size, num_pages)) return ATTN_ERR_INVALID_ARG;
     if (B <= 0 || h_q <= 0 || d_c <= 0 || d_r < 0) return ATTN_ERR_INVALID_ARG;
@@ -263,7 +270,7 @@ attn_status_t mla_decode_paged(const void *q, const void *kv_pages, void *o, flo
     float *ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                               align_up((size_t)B * h_q * ns * d_c * sizeof(float), 256));
     mi355::MlaArgs a{q, kv_pages, o, lse, seq_lens, B, S_max, h_q, d_c, d_r, scale, split, ns,
-                     ws_o, ws_lse, block_table, max_blocks, page_size, num_pages};
+                     ws_o, ws_lse, block_table, max_blocks, page_size, num_pages, sinks};
     return mi355::launch_mla_decode_bf16(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -394,11 +394,14 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
 // weights 2^(L_s - M) of the splits are computed once per lane (lane s holds
 // split s of a 64-split chunk) and broadcast with readlane, and the partial
 // rows of four splits are loaded before they are accumulated.
+// An optional sink logit per head (sinks[h], natural-log units like the
+// scaled scores) adds one more term to the merged denominator and carries no
+// value: Z = sum_s 2^(L_s - M) + 2^(sink log2 e - M).
 template <int DV>
 __global__ __launch_bounds__(256) void split_combine_kernel(const float *ws_o, const float *ws_lse,
                                                             const int32_t *seq_lens, __bf16 *o, float *lse,
                                                             int n_rows, int H, int S_max, int split,
-                                                            int n_split_max) {
+                                                            int n_split_max, const float *sinks) {
     constexpr int PER = DV / 64;                  // 2 or 8 values per lane
     typedef __attribute__((ext_vector_type(PER))) float fvec;
     const int lane = threadIdx.x & 63;
@@ -420,6 +423,8 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float *ws_o, c
     M = fmaxf(M, shfl_xor(M, 8));
     M = fmaxf(M, shfl_xor(M, 16));
     M = pair32_max(M);
+    const float sink2 = sinks ? sinks[row % H] * kLog2e : -INFINITY;
+    const float Mall = fmaxf(M, sink2);
 
     fvec acc;
 #pragma unroll
@@ -449,6 +454,12 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float *ws_o, c
                 acc += ws * v;
             }
         }
+    }
+    if (sinks && Mall != -INFINITY) {             // rescale to the common reference
+        const float f = M == -INFINITY ? 0.f : fast_exp2(M - Mall);
+        acc *= f;
+        Z = Z * f + fast_exp2(sink2 - Mall);
+        M = Mall;
     }
     const float inv = Z > 0.f ? 1.0f / Z : 0.f;
     __bf16 *dst = o + (size_t)row * DV + PER * lane;
@@ -516,12 +527,12 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_combine(a.ws_o, a.ws_lse, a.seq_lens, a.o, a.lse, a.B, a.hq, D, a.S_max,
-                                a.split, a.n_split_max, stream);
+                                a.split, a.n_split_max, a.sinks, stream);
 }
 
 hipError_t launch_split_combine(const float *ws_o, const float *ws_lse, const int32_t *seq_lens,
                                 void *o, float *lse, int B, int H, int dv, int S_max, int split,
-                                int n_split_max, hipStream_t stream) {
+                                int n_split_max, const float *sinks, hipStream_t stream) {
     const long long n_rows = (long long)B * H;
     if (n_rows > 0x7fffffffLL - 4) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((n_rows + 3) / 4));
@@ -529,11 +540,11 @@ hipError_t launch_split_combine(const float *ws_o, const float *ws_lse, const in
     switch (dv) {
         case 128:
             hipLaunchKernelGGL(split_combine_kernel<128>, grid, dim3(256), 0, stream, ws_o, ws_lse,
-                               seq_lens, ob, lse, (int)n_rows, H, S_max, split, n_split_max);
+                               seq_lens, ob, lse, (int)n_rows, H, S_max, split, n_split_max, sinks);
             break;
         case 512:
             hipLaunchKernelGGL(split_combine_kernel<512>, grid, dim3(256), 0, stream, ws_o, ws_lse,
-                               seq_lens, ob, lse, (int)n_rows, H, S_max, split, n_split_max);
+                               seq_lens, ob, lse, (int)n_rows, H, S_max, split, n_split_max, sinks);
             break;
         default: return hipErrorInvalidValue;
     }

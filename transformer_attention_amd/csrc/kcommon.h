@@ -128,6 +128,21 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// End of a row with a sink logit s2 (log2 units): the row's online-softmax
+// state is the reference max m (log2 units, -inf if no key was visible), the
+// sum l of 2^(x - m) over its keys and the output accumulated against m.  The
+// sink adds 2^s2 to the denominator and has no value row.  Returns the factor
+// that turns the accumulated output into O, and writes the natural-log
+// log-sum-exp of keys and sink.
+__device__ __forceinline__ float finish_row_with_sink(float m, float l, float s2, float &lse_nat) {
+    const float M = fmaxf(m, s2);
+    if (M == -INFINITY) { lse_nat = -INFINITY; return 0.f; }
+    const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    const float z = l * f + (s2 == -INFINITY ? 0.f : fast_exp2(s2 - M));
+    lse_nat = z > 0.f ? M * kLn2 + __logf(z) : -INFINITY;
+    return z > 0.f ? f / z : 0.f;
+}
+
 // acc + the sum of the eight bf16 values of v (v_dot2_f32_bf16 against (1, 1):
 // two values per instruction; bf16 values times 1 are exact).
 __device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {

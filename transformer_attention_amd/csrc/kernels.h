@@ -14,6 +14,7 @@ struct PrefillArgs {
     int B, T, hq, hkv, d;
     int causal, window;
     float scale;
+    const float *sinks;   // [hq] sink logits or nullptr
 };
 
 // bf16, d = 128, bf16 MFMA.  Returns hipSuccess or the launch error.
@@ -30,6 +31,8 @@ struct PrefillBwdArgs {
     float scale;
     float *ws_stats;      // [B * hq, Tpad, 2]: lse * log2(e) (+inf on pad rows), dout . o
     int Tpad;             // T rounded up to a multiple of 64
+    const float *sinks;   // [hq] sink logits or nullptr
+    float *dsinks;        // [hq] their gradient (written when non-null; needs sinks)
 };
 // bf16, d = 128: a row-statistics pass, then dK/dV (key-block parallel)
 // and dQ (query-block parallel).
@@ -54,6 +57,7 @@ struct DecodeArgs {
     // max_blocks * page_size
     const int32_t *block_table;
     int max_blocks, page_size, num_pages;
+    const float *sinks;   // [hq] sink logits or nullptr
 };
 hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream);
 
@@ -72,14 +76,16 @@ struct MlaArgs {
     // cache is [num_pages, page_size, d_c + d_r], S_max = max_blocks * page_size
     const int32_t *block_table;
     int max_blocks, page_size, num_pages;
+    const float *sinks;   // [H] sink logits or nullptr
 };
 hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream);
 
 // Merge of split partials: o[b,h,:] (bf16) and lse[b,h] (natural log, may be
-// null) from ws_o/ws_lse over the ceil(len_b / split) splits of sequence b.
+// null) from ws_o/ws_lse over the ceil(len_b / split) splits of sequence b;
+// sinks (per head, may be null) adds a sink logit to each merged denominator.
 hipError_t launch_split_combine(const float *ws_o, const float *ws_lse,
                                 const int32_t *seq_lens, void *o, float *lse,
                                 int B, int H, int dv, int S_max, int split,
-                                int n_split_max, hipStream_t stream);
+                                int n_split_max, const float *sinks, hipStream_t stream);
 
 }  // namespace mi355

@@ -365,7 +365,7 @@ hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_combine(a.ws_o, a.ws_lse, a.seq_lens, a.o, a.lse, a.B, a.H, DC, a.S_max,
-                                a.split, a.n_split_max, stream);
+                                a.split, a.n_split_max, a.sinks, stream);
 }
 
 }  // namespace mi355

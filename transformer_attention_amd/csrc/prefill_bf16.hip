@@ -93,6 +93,7 @@ struct Params {
     int n_head_groups;    // B * hkv * (G / hpw)
     int causal, window;
     float scale_log2;     // scale * log2(e)
+    const float *sinks;   // [hq] sink logits (natural units) or nullptr
 };
 
 // byte offset of (row, 16-byte chunk) inside a K tile / a V tile
@@ -542,7 +543,9 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
         const int row = row0 + 32 * nb;
         const float lt = pair32_sum(l_run[nb]);
         if (row >= T) continue;
-        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        float lse_sink = 0.f;
+        if (p.sinks) inv = finish_row_with_sink(m_run[nb], lt, p.sinks[h] * kLog2e, lse_sink);
         __bf16 *orow = p.o + q_base + (size_t)row * D;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -555,7 +558,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
             }
         if (p.lse && hi == 0) {
             const size_t li = ((size_t)b * p.hq + h) * (size_t)T + row;
-            p.lse[li] = lt > 0.f ? m_run[nb] * kLn2 + __logf(lt) : -INFINITY;
+            p.lse[li] = p.sinks ? lse_sink : (lt > 0.f ? m_run[nb] * kLn2 + __logf(lt) : -INFINITY);
         }
     }
 }
@@ -586,6 +589,7 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs &a, hipStream_t stream) {
     p.causal = a.causal;
     p.window = a.window;
     p.scale_log2 = a.scale * kLog2e;
+    p.sinks = a.sinks;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)prefill_bf16_d128_kernel<NB, KB, NST>,

@@ -74,7 +74,33 @@ struct Params {
     float scale, c;                          // c = scale * log2(e)
     // dq kernel decomposition (as the forward)
     int hpw, rows_per_wg, n_row_blocks, n_head_groups;
+    const float *sinks;
+    float *dsinks;
 };
+
+// ---------------------------------------------------------------------------
+// Gradient of a sink logit s_h (an extra softmax-denominator term without a
+// value row): dL/ds_h = -sum over the head's rows (every batch entry) of
+// exp(s_h - L_i) D_i, from the row statistics.  One workgroup per query
+// head; fixed summation order, so the result is reproducible.
+__global__ __launch_bounds__(256) void bwd_sink_grad_kernel(Params p) {
+    const int h = blockIdx.x;
+    const float s2 = p.sinks[h] * kLog2e;
+    float acc = 0.f;
+    for (int b = 0; b < p.B; ++b) {
+        const float *st = p.stats + 2 * ((size_t)b * p.hq + h) * p.Tpad;
+        for (int r = threadIdx.x; r < p.T; r += 256) {
+            const f32x2 v = *reinterpret_cast<const f32x2 *>(st + 2 * r);
+            acc = __builtin_fmaf(fast_exp2(s2 - v[0]), v[1], acc);
+        }
+    }
+    __shared__ float part[4];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) p.dsinks[h] = -((part[0] + part[1]) + (part[2] + part[3]));
+}
 
 // ---------------------------------------------------------------------------
 // Row statistics: D_i = dO_i . O_i and L_i log2(e); 16 lanes per row.
@@ -585,6 +611,8 @@ hipError_t launch_prefill_bwd_bf16_d128(const PrefillBwdArgs &a, hipStream_t str
     p.window = a.window;
     p.scale = a.scale;
     p.c = a.scale * kLog2e;
+    p.sinks = a.sinks;
+    p.dsinks = a.dsinks;
     p.hpw = (p.G % 8 == 0) ? 8 : (p.G % 4 == 0) ? 4 : (p.G % 2 == 0 ? 2 : 1);
     p.rows_per_wg = WG_ROWS / p.hpw;
     p.n_row_blocks = (a.T + p.rows_per_wg - 1) / p.rows_per_wg;
@@ -612,6 +640,9 @@ hipError_t launch_prefill_bwd_bf16_d128(const PrefillBwdArgs &a, hipStream_t str
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)n_b), dim3(64 * KB_WAVES), KB_LDS, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess || !a.dsinks) return e;
+    hipLaunchKernelGGL(bwd_sink_grad_kernel, dim3((unsigned)a.hq), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

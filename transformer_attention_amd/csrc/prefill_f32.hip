@@ -24,6 +24,7 @@ struct Params {
     int T, hq, hkv, G;
     int causal, window;
     float scale_log2;
+    const float *sinks;   // [hq] sink logits (natural units) or nullptr
 };
 
 template <int DH>
@@ -85,11 +86,12 @@ __global__ __launch_bounds__(ROWS) void prefill_f32_kernel(Params p) {
         __syncthreads();
     }
     if (row >= T) return;
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    float inv = l > 0.f ? 1.0f / l : 0.f;
+    float lse_out = l > 0.f ? m * kLn2 + __logf(l) : -INFINITY;
+    if (p.sinks) inv = finish_row_with_sink(m, l, p.sinks[h] * kLog2e, lse_out);
 #pragma unroll
     for (int d = 0; d < DH; ++d) p.o[q_base + (size_t)row * DH + d] = o[d] * inv;
-    if (p.lse)
-        p.lse[((size_t)b * p.hq + h) * (size_t)T + row] = l > 0.f ? m * kLn2 + __logf(l) : -INFINITY;
+    if (p.lse) p.lse[((size_t)b * p.hq + h) * (size_t)T + row] = lse_out;
 }
 
 }  // namespace
@@ -108,6 +110,7 @@ hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t stream) {
     p.causal = a.causal;
     p.window = a.window;
     p.scale_log2 = a.scale * kLog2e;
+    p.sinks = a.sinks;
     dim3 grid((a.T + ROWS - 1) / ROWS, a.hq, a.B);
     switch (a.d) {
         case 16: hipLaunchKernelGGL(prefill_f32_kernel<16>, grid, dim3(ROWS), 0, stream, p); break;
