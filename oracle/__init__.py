@@ -71,6 +71,14 @@ def _load():
     lib.oracle_decode.restype = I
     lib.oracle_mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, D, P]
     lib.oracle_mla_decode.restype = I
+    lib.oracle_fp8_e4m3_value.argtypes = [I]
+    lib.oracle_fp8_e4m3_value.restype = D
+    lib.oracle_fp8_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_fp8_e4m3_encode.restype = I
+    lib.oracle_quantize_kv_fp8.argtypes = [P, P, P, I, I, I, I]
+    lib.oracle_quantize_kv_fp8.restype = I
+    lib.oracle_decode_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, P]
+    lib.oracle_decode_fp8.restype = I
     lib.oracle_merge_partials.argtypes = [P, P, I, I, P, P]
     lib.oracle_merge_partials.restype = None
     lib.oracle_set_threads.argtypes = [I]
@@ -248,6 +256,78 @@ def mla_decode_paged(q, kv_pages, block_table, seq_lens, *, d_c: int, d_r: int, 
     """MLA decode on a paged cache: the contiguous MLA decode of the gathered cache."""
     c = gather_pages(_f32(kv_pages), block_table, seq_lens, head_axis=False)
     return mla_decode(q, c, seq_lens, d_c=d_c, d_r=d_r, scale=scale)
+
+
+def fp8_e4m3_value(code: int) -> float:
+    """Value of an OCP FP8 E4M3 code (NaN for 0x7f / 0xff)."""
+    return float(_load().oracle_fp8_e4m3_value(int(code)))
+
+
+def fp8_e4m3_encode(v: float) -> int:
+    """Nearest E4M3 code to the float32 value v (ties to even, saturating)."""
+    return int(_load().oracle_fp8_e4m3_encode(float(np.float32(v))))
+
+
+def fp8_dequantize(codes, scales, *, tile: int = 32) -> np.ndarray:
+    """codes:[..., S, d] uint8, scales:[..., ceil(S/tile)] -> float64 values."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    table = np.array([fp8_e4m3_value(c) for c in range(256)], dtype=np.float64)
+    sc = np.repeat(np.asarray(scales, dtype=np.float64), tile, axis=-1)[..., :codes.shape[-2]]
+    return table[codes] * sc[..., None]
+
+
+def quantize_kv_fp8(x):
+    """Per-tile FP8 quantisation of a cache x:[B, h_kv, S, d]: 32 positions of
+    one head per tile, scale = amax / 448.  Returns (codes uint8 like x,
+    scales float32 [B, h_kv, ceil(S/32)])."""
+    x = _f32(x)
+    B, hkv, S, d = x.shape
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scales = np.zeros((B, hkv, (S + 31) // 32), dtype=np.float32)
+    rc = _load().oracle_quantize_kv_fp8(_ptr(x), _ptr(codes), _ptr(scales), B, hkv, S, d)
+    if rc != 0:
+        raise ValueError("oracle_quantize_kv_fp8: invalid shape")
+    return codes, scales
+
+
+def decode_fp8(q, k8, v8, k_scales, v_scales, seq_lens, *, window: int = 0, scale: float,
+               sinks=None):
+    """Decode against an FP8 cache (codes [B,h_kv,S_max,d], per-tile scales
+    [B,h_kv,ceil(S_max/32)]): the plain decode of the dequantised cache."""
+    q = _f32(q)
+    B, hq = q.shape[0], q.shape[1]
+    d = q.shape[-1]
+    k8 = np.ascontiguousarray(np.asarray(k8, dtype=np.uint8))
+    v8 = np.ascontiguousarray(np.asarray(v8, dtype=np.uint8))
+    _, hkv, S_max, d2 = k8.shape
+    assert d2 == d and v8.shape == k8.shape
+    ks, vs = _f32(k_scales), _f32(v_scales)
+    assert ks.shape == (B, hkv, (S_max + 31) // 32) and vs.shape == ks.shape
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    o = np.zeros((B, hq, d), dtype=np.float64)
+    lse = np.zeros((B, hq), dtype=np.float64)
+    sk, sk_ptr = _sinks(sinks, hq)
+    rc = _load().oracle_decode_fp8(_ptr(np.ascontiguousarray(q.reshape(B, hq, d))), _ptr(k8),
+                                   _ptr(v8), _ptr(ks), _ptr(vs), _ptr(lens), _ptr(o), _ptr(lse),
+                                   B, S_max, hq, hkv, d, int(window), float(scale), sk_ptr)
+    if rc != 0:
+        raise ValueError("oracle_decode_fp8: invalid shape")
+    return o, lse
+
+
+def decode_paged_fp8(q, k8_pages, v8_pages, k_scale_pages, v_scale_pages, block_table, seq_lens,
+                     *, window: int = 0, scale: float, sinks=None):
+    """FP8 decode on a paged cache: codes [num_pages, h_kv, page_size, d], scales
+    [num_pages, h_kv, page_size / 32]; gathered, then decode_fp8."""
+    ps = np.asarray(k8_pages).shape[2]
+    lens = np.asarray(seq_lens)
+    k8 = gather_pages(k8_pages, block_table, lens, head_axis=True)
+    v8 = gather_pages(v8_pages, block_table, lens, head_axis=True)
+    lens_t = (np.maximum(lens, 0) + 31) // 32
+    ks = gather_pages(_f32(k_scale_pages)[..., None], block_table, lens_t, head_axis=True)[..., 0]
+    vs = gather_pages(_f32(v_scale_pages)[..., None], block_table, lens_t, head_axis=True)[..., 0]
+    assert ks.shape[2] * 32 == k8.shape[2] and ps % 32 == 0
+    return decode_fp8(q, k8, v8, ks, vs, lens, window=window, scale=scale, sinks=sinks)
 
 
 def merge_partials(parts_o, parts_lse):

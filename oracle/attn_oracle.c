@@ -64,29 +64,53 @@ static int prefill_visible(long i, long j, int causal, int window)
  * with no value row ("Attention Engineering ...", section 5, failure mode
  * 2: a learnable scalar sink logit in the denominator).
  * Writes out[0..dv) and *lse. */
-static void softmax_mix(const double *s, const unsigned char *vis, long n,
-                        const float *v, long vstride, int dv,
-                        double *out, double *lse, double *p, double sink)
+static void softmax_weights(const double *s, const unsigned char *vis, long n,
+                            double *p, double *lse, double sink)
 {
     double m = -INFINITY;
     long any = 0;
     for (long j = 0; j < n; ++j)
         if (vis[j]) { if (!any || s[j] > m) m = s[j]; any = 1; }
-    for (int d = 0; d < dv; ++d) out[d] = 0.0;
     if (sink != -INFINITY && (!any || sink > m)) m = sink;
-    if (!any) { *lse = sink; return; }
+    if (!any) {
+        for (long j = 0; j < n; ++j) p[j] = 0.0;
+        *lse = sink;
+        return;
+    }
     double l = sink != -INFINITY ? exp(sink - m) : 0.0;
     for (long j = 0; j < n; ++j) {
         p[j] = vis[j] ? exp(s[j] - m) : 0.0;
         l += p[j];
     }
+    for (long j = 0; j < n; ++j) p[j] /= l;
+    *lse = m + log(l);
+}
+
+static void softmax_mix(const double *s, const unsigned char *vis, long n,
+                        const float *v, long vstride, int dv,
+                        double *out, double *lse, double *p, double sink)
+{
+    softmax_weights(s, vis, n, p, lse, sink);
+    for (int d = 0; d < dv; ++d) out[d] = 0.0;
     for (long j = 0; j < n; ++j) {
         if (!vis[j]) continue;
-        const double w = p[j] / l;
         const float *vr = v + j * vstride;
-        for (int d = 0; d < dv; ++d) out[d] += w * (double)vr[d];
+        for (int d = 0; d < dv; ++d) out[d] += p[j] * (double)vr[d];
     }
-    *lse = m + log(l);
+}
+
+/* the same with double value rows */
+static void softmax_mix_d(const double *s, const unsigned char *vis, long n,
+                          const double *v, long vstride, int dv,
+                          double *out, double *lse, double *p, double sink)
+{
+    softmax_weights(s, vis, n, p, lse, sink);
+    for (int d = 0; d < dv; ++d) out[d] = 0.0;
+    for (long j = 0; j < n; ++j) {
+        if (!vis[j]) continue;
+        const double *vr = v + j * vstride;
+        for (int d = 0; d < dv; ++d) out[d] += p[j] * vr[d];
+    }
 }
 
 /*
@@ -424,4 +448,134 @@ int oracle_max_threads(void)
 #else
     return 1;
 #endif
+}
+
+/*
+ * FP8 KV cache.
+ *
+ * Format: OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits (bias 7),
+ * 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); no infinities; the
+ * all-ones magnitude 0x7f is NaN; the largest finite value is 448.  This is
+ * the FP8 type of the pages' per-tile quantisation ("Flash Attention 3 and
+ * Multi-Headed Latent Attention", the FP8 attention section: the scale is
+ * the tile's absolute maximum over 448, the E4M3 maximum) and of the
+ * quantised caches the pages name ("Attention deep dive ...", section 5,
+ * production-engine notes; "2.4 Multi-Head Attention, MQA, GQA & MLA": an
+ * fp8 cache stacks with GQA).
+ *
+ * Tile of the cache (reading): 32 consecutive positions of one K/V head of
+ * one sequence, all d_h values of each; one fp32 scale per tile and per
+ * tensor (K and V separately).  scale = amax / 448 (fp32 division; 1 for an
+ * all-zero tile), code = nearest E4M3 value of x / scale (fp32 division),
+ * ties to the even code, magnitudes above 448 saturated to 448.
+ */
+static double fp8_value(unsigned code)
+{
+    const unsigned e = (code >> 3) & 15u, m = code & 7u;
+    const double sgn = (code & 0x80u) ? -1.0 : 1.0;
+    if (e == 15u && m == 7u) return NAN;
+    if (e == 0u) return sgn * ldexp((double)m / 8.0, -6);
+    return sgn * ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+}
+
+double oracle_fp8_e4m3_value(int code) { return fp8_value((unsigned)code & 0xffu); }
+
+/* nearest finite E4M3 code to v, ties to the even code, saturating */
+static unsigned char fp8_encode(float v)
+{
+    const double a = fabs((double)v);
+    unsigned best = 0;
+    double best_err = INFINITY;
+    for (unsigned c = 0; c < 127u; ++c) {        /* every finite non-negative code */
+        const double err = fabs(fp8_value(c) - a);
+        if (err < best_err || (err == best_err && (c & 1u) == 0u)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    if (a >= 448.0) best = 126u;                 /* saturate */
+    return (unsigned char)(best | (signbit(v) ? 0x80u : 0u));
+}
+
+int oracle_fp8_e4m3_encode(float v) { return (int)fp8_encode(v); }
+
+/* x:[B,hkv,S,d] float -> codes:[B,hkv,S,d], scales:[B,hkv,ceil(S/32)] */
+int oracle_quantize_kv_fp8(const float *x, unsigned char *codes, float *scales,
+                           int B, int hkv, int S, int d)
+{
+    if (B < 0 || hkv <= 0 || S < 0 || d <= 0) return -1;
+    const long nt = (S + 31) / 32;
+    const long tiles = (long)B * hkv * nt;
+#pragma omp parallel for schedule(static)
+    for (long u = 0; u < tiles; ++u) {
+        const long t = u % nt, bg = u / nt;
+        const long r0 = t * 32, r1 = (r0 + 32 < S) ? r0 + 32 : S;
+        const float *xb = x + (bg * (long)S) * d;
+        unsigned char *cb = codes + (bg * (long)S) * d;
+        float amax = 0.0f;
+        for (long r = r0; r < r1; ++r)
+            for (int e = 0; e < d; ++e) {
+                const float a = fabsf(xb[r * d + e]);
+                if (a > amax) amax = a;
+            }
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        scales[u] = sc;
+        for (long r = r0; r < r1; ++r)
+            for (int e = 0; e < d; ++e) {
+                const float y = xb[r * d + e] / sc;
+                cb[r * d + e] = fp8_encode(y);
+            }
+    }
+    return 0;
+}
+
+/*
+ * Decode against an FP8 cache: the plain decode (see oracle_decode) on the
+ * dequantised values code * scale of the cache tile, in double.
+ * k8, v8:[B,hkv,S_max,d] codes; ks, vs:[B,hkv,ceil(S_max/32)] scales.
+ */
+int oracle_decode_fp8(const float *q, const unsigned char *k8, const unsigned char *v8,
+                      const float *ks, const float *vs, const int *seq_lens,
+                      double *o, double *lse, int B, int S_max, int hq, int hkv, int d,
+                      int window, double scale, const float *sinks)
+{
+    if (B < 0 || S_max < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv) return -1;
+    const int G = hq / hkv;
+    const long nt = (S_max + 31) / 32;
+    const long units = (long)B * hq;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (S_max > 0 ? S_max : 1));
+        double *p = (double *)malloc(sizeof(double) * (S_max > 0 ? S_max : 1));
+        unsigned char *vis = (unsigned char *)malloc(S_max > 0 ? S_max : 1);
+        double *vdq = (double *)malloc(sizeof(double) * ((long)(S_max > 0 ? S_max : 1) * d));
+#pragma omp for schedule(dynamic, 1)
+        for (long u = 0; u < units; ++u) {
+            const long h = u % hq, b = u / hq, g = h / G;
+            long len = seq_lens[b];
+            if (len < 0) len = 0;
+            if (len > S_max) len = S_max;
+            const long i = len - 1;
+            const float *qi = q + (b * hq + h) * (long)d;
+            const long bg = b * hkv + g;
+            const unsigned char *kb = k8 + (bg * (long)S_max) * d;
+            const unsigned char *vb = v8 + (bg * (long)S_max) * d;
+            for (long j = 0; j < len; ++j) {
+                const double ksc = (double)ks[bg * nt + j / 32];
+                const double vsc = (double)vs[bg * nt + j / 32];
+                double acc = 0.0;
+                for (int t = 0; t < d; ++t)
+                    acc += (double)qi[t] * (fp8_value(kb[j * d + t]) * ksc);
+                s[j] = acc * scale;
+                vis[j] = (unsigned char)(window <= 0 || i - j < window);
+                for (int t = 0; t < d; ++t) vdq[j * d + t] = fp8_value(vb[j * d + t]) * vsc;
+            }
+            double l_out;
+            softmax_mix_d(s, vis, len, vdq, d, d, o + u * d, &l_out, p,
+                          sinks ? (double)sinks[h] : -INFINITY);
+            if (lse) lse[u] = l_out;
+        }
+        free(s); free(p); free(vis); free(vdq);
+    }
+    return 0;
 }
