@@ -21,7 +21,8 @@ two device synchronisations; kernel durations come from HIP events recorded
 on the stream the kernels run on.  One JSON line is printed.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|backward|decode|decode-paged|mla|swa-mha|swa-mqa|copy]
+                    [--only prefill|backward|decode|decode-paged|decode-fp8|mla|swa-mha|
+                            swa-mqa|copy]
 
 ``--only copy`` times a plain 1 GiB device copy instead: it is the
 calibration run for rocprofv3's HBM byte counters, not an attention bench.
@@ -160,6 +161,32 @@ def bench_decode_paged(torch, ta, W, steps, warmup, page_size=64):
             "frac_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
+def bench_decode_fp8(torch, ta, W, steps, warmup):
+    """The 70B decode against the same cache quantised to FP8 (E4M3, one scale
+    per 32 positions of a head): half the cache bytes."""
+    s = W.GQA70B_DECODE
+    q, kc, vc, lens = W.decode_inputs(s, seed=0, device="cuda", gen_device="cuda")
+    k8, ks = ta.attn_quantize_kv_fp8(kc)
+    del kc
+    v8, vs = ta.attn_quantize_kv_fp8(vc)
+    del vc
+    lens_d = lens.to("cuda")
+    o = torch.empty_like(q)
+    ws = torch.empty(ta.attn_decode_workspace_size(s.B, s.S_max, s.h_q, s.h_kv, s.d_h),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = lambda: ta.attn_decode_fp8(q, k8, v8, ks, vs, lens_d, scale=s.scale, o=o, workspace=ws)
+    ms, wall = _events_time(torch, fn, steps, warmup, stream)
+    total_len = int(lens.sum())
+    tiles = int(((lens + 31) // 32).sum())
+    nbytes = (total_len * 2 * s.h_kv * s.d_h + tiles * 2 * s.h_kv * 4 +
+              2 * s.B * s.h_q * s.d_h * 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del q, k8, v8, ks, vs, o, ws
+    return {"ms": ms, "wall_s": wall, "bytes": nbytes, "gbs": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+
+
 def bench_copy(torch, steps, warmup, nbytes=1 << 30):
     """A plain device-to-device copy of known size (reads and writes nbytes
     each).  Not part of the attention path: its HBM counter readings give the
@@ -239,7 +266,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    choices=["prefill", "backward", "decode", "decode-paged", "mla", "swa-mha",
+                    choices=["prefill", "backward", "decode", "decode-paged", "decode-fp8", "mla",
+                             "swa-mha",
                              "swa-mqa", "copy"])
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -278,6 +306,10 @@ def main(argv=None):
         out["decode"] = bench_decode(torch, ta, W, args.steps, args.warmup)
         print(f"[bench] decode {out['decode']['ms']:.3f} ms {out['decode']['gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
+    if only in (None, "decode-fp8"):
+        out["decode_fp8"] = bench_decode_fp8(torch, ta, W, args.steps, args.warmup)
+        print(f"[bench] decode (fp8 cache) {out['decode_fp8']['ms']:.3f} ms "
+              f"{out['decode_fp8']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     if only in (None, "decode-paged"):
         out["decode_paged"] = bench_decode_paged(torch, ta, W, args.steps, args.warmup)
         print(f"[bench] decode (paged) {out['decode_paged']['ms']:.3f} ms "
@@ -338,6 +370,14 @@ def main(argv=None):
                                             f"{d['page_size']} positions (random page order)",
                                 "ms": round(d["ms"], 4), "GB_s": round(d["gbs"], 1),
                                 "frac_hbm_peak": round(d["frac_hbm_peak"], 4), "bytes": d["bytes"]}
+    if "decode_fp8" in out and next(iter(out)) != "decode_fp8":
+        d = out["decode_fp8"]
+        line["decode_fp8"] = {"workload": "70B-shaped GQA decode, cache in FP8 E4M3 (one scale per "
+                                          "32 positions of a head)",
+                              "ms": round(d["ms"], 4), "GB_s": round(d["gbs"], 1),
+                              "frac_hbm_peak": round(d["frac_hbm_peak"], 4), "bytes": d["bytes"]}
+        if "decode" in out:
+            line["decode_fp8"]["speedup_vs_bf16_cache"] = round(out["decode"]["ms"] / d["ms"], 3)
     if "backward" in out and next(iter(out)) != "backward":
         r = out["backward"]
         line["backward"] = {"workload": "Llama-3-8B-shaped causal GQA prefill backward (dQ, dK, dV)",

@@ -246,6 +246,60 @@ attn_status_t mla_decode_paged(const void *q, const void *kv_pages, void *o, flo
                                int split_tokens, void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/*
+ * FP8 KV cache -- the decode steps against a cache quantised to OCP FP8 E4M3
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest value 448,
+ * no infinities), half the bytes of bf16.  The pages quantise per tile with
+ * scale = amax / 448 and cast x / scale to E4M3 ("Flash Attention 3 and
+ * Multi-Headed Latent Attention", the FP8 attention section), and name the
+ * quantised cache as what production engines keep ("Attention deep dive
+ * ...", section 5, production-engine notes; "2.4 Multi-Head Attention, MQA,
+ * GQA & MLA": an fp8 cache stacks with GQA).
+ *
+ * Tile: 32 consecutive positions of one K/V head of one sequence (or page),
+ * all d_h values; one fp32 scale per tile, separately for K and for V.  The
+ * cached value is code * scale.
+ *
+ * attn_quantize_kv_fp8 -- writes such a cache from a bf16 one:
+ *   x      : [B, h_kv, S, d_h] bf16 (read)
+ *   codes  : [B, h_kv, S, d_h] uint8 E4M3 codes (written)
+ *   scales : [B, h_kv, ceil(S / 32)] float32 (written)
+ * scale = amax / 448 over the tile (1 for an all-zero tile, fp32 division);
+ * code = E4M3 nearest to x / scale (fp32 division, ties to even, magnitudes
+ * clamped to 448).  The last tile may hold fewer than 32 positions.  A paged
+ * cache [num_pages, h_kv, page_size, d_h] is quantised by passing B =
+ * num_pages, S = page_size.  d_h must be a multiple of 8.
+ *
+ * attn_decode_fp8 / attn_decode_paged_fp8 -- attn_decode / attn_decode_paged
+ * with k_cache / v_cache (or the pages) holding codes and k_scales / v_scales
+ * their tile scales:
+ *   contiguous : [B, h_kv, ceil(S_max / 32)]
+ *   paged      : [num_pages, h_kv, page_size / 32]
+ * (the layouts attn_quantize_kv_fp8 writes).  The result is attention over
+ * the dequantised cache: the codes are widened to bf16 exactly, the K scale
+ * multiplies the scores of its tile and the V scale the weights of its
+ * tile's values, accumulation as in attn_decode.  Everything else
+ * (arguments, workspace, errors) is as in attn_decode / attn_decode_paged;
+ * null k_scales or v_scales is ATTN_ERR_INVALID_ARG.
+ */
+attn_status_t attn_quantize_kv_fp8(const void *x, void *codes, float *scales,
+                                   int B, int h_kv, int S, int d_h, hipStream_t stream);
+attn_status_t attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                              const float *k_scales, const float *v_scales,
+                              void *o, float *lse, const int32_t *seq_lens,
+                              int B, int S_max, int h_q, int h_kv, int d_h,
+                              int window, float scale, const float *sinks, int split_tokens,
+                              void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+attn_status_t attn_decode_paged_fp8(const void *q, const void *k_pages, const void *v_pages,
+                                    const float *k_scales, const float *v_scales,
+                                    void *o, float *lse, const int32_t *seq_lens,
+                                    const int32_t *block_table, int B, int max_blocks,
+                                    int page_size, int num_pages, int h_q, int h_kv, int d_h,
+                                    int window, float scale, const float *sinks,
+                                    int split_tokens, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *attn_status_string(attn_status_t status);
 

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for n in ("attn_prefill", "attn_prefill_backward", "attn_prefill_backward_workspace_size",
               "attn_decode", "mla_decode", "attn_decode_workspace_size",
               "attn_decode_paged", "attn_decode_paged_workspace_size", "mla_decode_paged",
-              "mla_decode_paged_workspace_size",
+              "mla_decode_paged_workspace_size", "attn_quantize_kv_fp8", "attn_decode_fp8",
+              "attn_decode_paged_fp8",
               "mla_decode_workspace_size", "attn_status_string", "attn_abi_version"):
         assert n in names, n
 
@@ -125,6 +126,46 @@ def test_decode_validation(lib):
     assert need > 0
     assert dec(wsb=need - 1) == 3
     assert lib.attn_decode_workspace_size(2, 64, 7, 2, 128, 0) == 0
+
+
+def test_fp8_validation(lib):
+    def quant(**kw):
+        a = dict(x=FAKE, c=FAKE, s=FAKE, B=2, hkv=2, S=100, d=128)
+        a.update(kw)
+        return lib.attn_quantize_kv_fp8(a["x"], a["c"], a["s"], a["B"], a["hkv"], a["S"], a["d"],
+                                        None)
+    assert quant(x=None) == 1
+    assert quant(s=None) == 1
+    assert quant(S=0) == 1
+    assert quant(d=12) == 2                          # d_h must be a multiple of 8
+
+    def dec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, o=FAKE, lens=FAKE, B=2, S=64, hq=8,
+                 hkv=2, d=128, window=0, scale=0.1, split=0, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.attn_decode_fp8(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["o"], None,
+                                   a["lens"], a["B"], a["S"], a["hq"], a["hkv"], a["d"],
+                                   a["window"], a["scale"], None, a["split"], a["ws"], a["wsb"],
+                                   None)
+    assert dec(ks=None) == 1
+    assert dec(vs=None) == 1
+    assert dec(hq=7) == 1
+    assert dec(d=64) == 2
+    assert dec(ws=None) == 3
+
+    def pdec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, o=FAKE, lens=FAKE, bt=FAKE, B=2, mb=8,
+                 ps=64, np_=16, hq=8, hkv=2, d=128, window=0, scale=0.1, split=0, ws=FAKE,
+                 wsb=1 << 30)
+        a.update(kw)
+        return lib.attn_decode_paged_fp8(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["o"], None,
+                                         a["lens"], a["bt"], a["B"], a["mb"], a["ps"], a["np_"],
+                                         a["hq"], a["hkv"], a["d"], a["window"], a["scale"], None,
+                                         a["split"], a["ws"], a["wsb"], None)
+    assert pdec(ks=None) == 1
+    assert pdec(bt=None) == 1
+    assert pdec(ps=48) == 2
+    assert pdec(ws=None) == 3
 
 
 def test_paged_validation(lib):

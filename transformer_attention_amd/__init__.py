@@ -44,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "attn_decode", "attn_decode_workspace_size",
     "mla_decode", "mla_decode_workspace_size", "attn_decode_paged",
     "attn_decode_paged_workspace_size", "mla_decode_paged", "mla_decode_paged_workspace_size",
+    "attn_quantize_kv_fp8", "attn_decode_fp8", "attn_decode_paged_fp8",
     "attn_status_string",
     "attn_abi_version",
 )
@@ -92,6 +93,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_paged_workspace_size.restype = Z
     lib.mla_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, I, P, Z, P]
     lib.mla_decode_paged.restype = I
+    lib.attn_quantize_kv_fp8.argtypes = [P, P, P, I, I, I, I, P]
+    lib.attn_quantize_kv_fp8.restype = I
+    lib.attn_decode_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, I, P, Z, P]
+    lib.attn_decode_fp8.restype = I
+    lib.attn_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P,
+                                          I, P, Z, P]
+    lib.attn_decode_paged_fp8.restype = I
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -406,4 +414,113 @@ def mla_decode_paged(q, kv_pages, seq_lens, block_table, *, d_c: int = 512, d_r:
                               int(split_tokens), _ptr(workspace), ws_bytes,
                               _stream(q.device))
     _check(st, "mla_decode_paged")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_quantize_kv_fp8(x, *, codes=None, scales=None):
+    """Per-tile FP8 (E4M3) quantisation of a bf16 cache x:[B,h_kv,S,d] (or pages
+    [num_pages,h_kv,page_size,d]): tiles of 32 positions of one head, scale =
+    amax / 448.  Returns (codes uint8 like x, scales fp32 [B,h_kv,ceil(S/32)])."""
+    lib = load_library()
+    _require(x, "x", torch.bfloat16, ndim=4)
+    B, hkv, S, d = x.shape
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if codes is None else codes
+    nt = (S + 31) // 32
+    scales = torch.empty((B, hkv, nt), dtype=torch.float32, device=x.device) if scales is None else scales
+    _require(codes, "codes", torch.uint8, x.device)
+    _require(scales, "scales", torch.float32, x.device)
+    if tuple(codes.shape) != tuple(x.shape) or scales.numel() != B * hkv * nt:
+        raise ValueError("codes / scales shape mismatch")
+    st = lib.attn_quantize_kv_fp8(_ptr(x), _ptr(codes), _ptr(scales), B, hkv, S, d,
+                                  _stream(x.device))
+    _check(st, "attn_quantize_kv_fp8")
+    return codes, scales
+
+
+def _decode_out(q, B, hq, o, lse, return_lse):
+    o = torch.empty_like(q) if o is None else o
+    _require(o, "o", torch.bfloat16, q.device)
+    if o.numel() != q.numel():
+        raise ValueError("o shape mismatch")
+    if lse is None and return_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, q.device)
+        if lse.numel() != B * hq:
+            raise ValueError("lse shape mismatch")
+    return o, lse
+
+
+def attn_decode_fp8(q, k_codes, v_codes, k_scales, v_scales, seq_lens, *, window: int = 0,
+                    scale=None, sinks=None, split_tokens: int = 0, o=None, lse=None,
+                    workspace=None, return_lse: bool = False):
+    """Decode against an FP8 cache: q:[B,h_q,d] or [B,h_q,1,d] bf16; codes:[B,h_kv,S_max,d]
+    uint8 (E4M3); scales:[B,h_kv,ceil(S_max/32)] fp32 (attn_quantize_kv_fp8's layout)."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16)
+    _require(k_codes, "k_codes", torch.uint8, q.device, 4)
+    _require(v_codes, "v_codes", torch.uint8, q.device, 4)
+    _require(seq_lens, "seq_lens", torch.int32, q.device, 1)
+    B, hkv, S_max, d = k_codes.shape
+    nt = (S_max + 31) // 32
+    for t, name in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        _require(t, name, torch.float32, q.device)
+        if t.numel() != B * hkv * nt:
+            raise ValueError(f"{name} must hold [B, h_kv, ceil(S_max/32)] values")
+    if tuple(v_codes.shape) != tuple(k_codes.shape):
+        raise ValueError("v_codes shape mismatch")
+    hq = q.shape[1]
+    if q.numel() != B * hq * d or q.shape[0] != B or q.shape[-1] != d or seq_lens.shape[0] != B:
+        raise ValueError("q / seq_lens shape mismatch")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o, lse = _decode_out(q, B, hq, o, lse, return_lse)
+    need = lib.attn_decode_workspace_size(B, S_max, hq, hkv, d, int(split_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", None, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_decode_fp8(_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scales),
+                             _ptr(v_scales), _ptr(o), _ptr(lse), _ptr(seq_lens), B, S_max, hq,
+                             hkv, d, int(window), float(scale), _ptr(_sinks(sinks, hq, q.device)),
+                             int(split_tokens), _ptr(workspace), ws_bytes, _stream(q.device))
+    _check(st, "attn_decode_fp8")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_decode_paged_fp8(q, k_pages, v_pages, k_scales, v_scales, seq_lens, block_table, *,
+                          window: int = 0, scale=None, sinks=None, split_tokens: int = 0,
+                          o=None, lse=None, workspace=None, return_lse: bool = False):
+    """FP8 decode on a paged cache: pages:[num_pages,h_kv,page_size,d] uint8 codes,
+    scales:[num_pages,h_kv,page_size/32] fp32; block_table int32[B,max_blocks]."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16)
+    _require(k_pages, "k_pages", torch.uint8, q.device, 4)
+    _require(v_pages, "v_pages", torch.uint8, q.device, 4)
+    _require(seq_lens, "seq_lens", torch.int32, q.device, 1)
+    _require(block_table, "block_table", torch.int32, q.device, 2)
+    num_pages, hkv, page_size, d = k_pages.shape
+    if tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("v_pages shape mismatch")
+    for t, name in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        _require(t, name, torch.float32, q.device)
+        if t.numel() != num_pages * hkv * (page_size // 32):
+            raise ValueError(f"{name} must hold [num_pages, h_kv, page_size/32] values")
+    B, max_blocks = block_table.shape
+    hq = q.shape[1]
+    if q.numel() != B * hq * d or q.shape[0] != B or q.shape[-1] != d or seq_lens.shape[0] != B:
+        raise ValueError("q / seq_lens shape mismatch")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o, lse = _decode_out(q, B, hq, o, lse, return_lse)
+    need = lib.attn_decode_paged_workspace_size(B, max_blocks, page_size, hq, hkv, d,
+                                                int(split_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", None, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_decode_paged_fp8(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scales),
+                                   _ptr(v_scales), _ptr(o), _ptr(lse), _ptr(seq_lens),
+                                   _ptr(block_table), B, max_blocks, page_size, num_pages, hq, hkv,
+                                   d, int(window), float(scale), _ptr(_sinks(sinks, hq, q.device)),
+                                   int(split_tokens), _ptr(workspace), ws_bytes, _stream(q.device))
+    _check(st, "attn_decode_paged_fp8")
     return (o, lse) if (return_lse or lse is not None) else o

@@ -144,12 +144,16 @@ size_t attn_decode_workspace_size(int B, int S_max, int h_q, int h_kv, int d_h, 
     return split_ws_bytes((long long)B * h_q, ns, d_h) + align_up((size_t)(B + 1) * sizeof(int32_t), 256);
 }
 
-attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *o,
-                          float *lse, const int32_t *seq_lens, int B, int S_max, int h_q,
-                          int h_kv, int d_h, int window, float scale, const float *sinks,
-                          int split_tokens, void *workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
-    if (bad_ptr(q) || bad_ptr(k_cache) || bad_ptr(v_cache) || bad_ptr(o) || bad_ptr(seq_lens))
+// Shared by the four GQA decode entry points (contiguous / paged, bf16 /
+// FP8): everything after the layout-specific checks.
+static attn_status_t decode_launch(const void *q, const void *k, const void *v, const float *k_scales,
+                                   const float *v_scales, void *o, float *lse,
+                                   const int32_t *seq_lens, const int32_t *block_table, int B,
+                                   int S_max, int max_blocks, int page_size, int num_pages, int h_q,
+                                   int h_kv, int d_h, int window, float scale, const float *sinks,
+                                   int split_tokens, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(o) || bad_ptr(seq_lens))
         return ATTN_ERR_INVALID_ARG;
     if (B <= 0 || S_max <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
     if (h_q % h_kv != 0 || window < 0 || !isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_INVALID_ARG;
@@ -164,10 +168,32 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     char *ws_end = static_cast<char *>(workspace) + align_up((size_t)B * h_q * ns * d_h * sizeof(float), 256);
     float *ws_lse = reinterpret_cast<float *>(ws_end);
     int32_t *plan = reinterpret_cast<int32_t *>(ws_end + align_up((size_t)B * h_q * ns * sizeof(float), 256));
-    mi355::DecodeArgs a{q, k_cache, v_cache, o, lse, seq_lens, B, S_max, h_q, h_kv, d_h,
+    mi355::DecodeArgs a{q, k, v, o, lse, seq_lens, B, S_max, h_q, h_kv, d_h,
                         window, scale, split, ns, ws_o, ws_lse, plan, device_cu_count(),
-                        nullptr, 0, 0, 0, sinks};
+                        block_table, max_blocks, page_size, num_pages, sinks, k_scales, v_scales};
     return mi355::launch_decode_bf16_d128(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *o,
+                          float *lse, const int32_t *seq_lens, int B, int S_max, int h_q,
+                          int h_kv, int d_h, int window, float scale, const float *sinks,
+                          int split_tokens, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    return decode_launch(q, k_cache, v_cache, nullptr, nullptr, o, lse, seq_lens, nullptr, B, S_max,
+                         0, 0, 0, h_q, h_kv, d_h, window, scale, sinks, split_tokens, workspace,
+                         workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                              const float *k_scales, const float *v_scales, void *o, float *lse,
+                              const int32_t *seq_lens, int B, int S_max, int h_q, int h_kv,
+                              int d_h, int window, float scale, const float *sinks,
+                              int split_tokens, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    if (bad_ptr(k_scales) || bad_ptr(v_scales)) return ATTN_ERR_INVALID_ARG;
+    return decode_launch(q, k_cache, v_cache, k_scales, v_scales, o, lse, seq_lens, nullptr, B,
+                         S_max, 0, 0, 0, h_q, h_kv, d_h, window, scale, sinks, split_tokens,
+                         workspace, workspace_bytes, stream);
 }
 
 size_t attn_decode_paged_workspace_size(int B, int max_blocks, int page_size, int h_q, int h_kv,
@@ -181,35 +207,56 @@ static bool bad_pages(const int32_t *block_table, int max_blocks, int page_size,
            (long long)max_blocks * page_size > 0x7fffffffLL;
 }
 
+static attn_status_t decode_paged_launch(const void *q, const void *k_pages, const void *v_pages,
+                                         const float *k_scales, const float *v_scales, void *o,
+                                         float *lse, const int32_t *seq_lens,
+                                         const int32_t *block_table, int B, int max_blocks,
+                                         int page_size, int num_pages, int h_q, int h_kv, int d_h,
+                                         int window, float scale, const float *sinks,
+                                         int split_tokens, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+    if (bad_pages(block_table, max_blocks, page_size, num_pages)) return ATTN_ERR_INVALID_ARG;
+    if (B <= 0) return ATTN_ERR_INVALID_ARG;
+    if (page_size % 32) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * max_blocks > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+    return decode_launch(q, k_pages, v_pages, k_scales, v_scales, o, lse, seq_lens, block_table, B,
+                         max_blocks * page_size, max_blocks, page_size, num_pages, h_q, h_kv, d_h,
+                         window, scale, sinks, split_tokens, workspace, workspace_bytes, stream);
+}
+
 attn_status_t attn_decode_paged(const void *q, const void *k_pages, const void *v_pages, void *o,
                                 float *lse, const int32_t *seq_lens, const int32_t *block_table,
                                 int B, int max_blocks, int page_size, int num_pages, int h_q,
                                 int h_kv, int d_h, int window, float scale, const float *sinks,
                                 int split_tokens, void *workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
-    if (bad_ptr(q) || bad_ptr(k_pages) || bad_ptr(v_pages) || bad_ptr(o) || bad_ptr(seq_lens))
-        return ATTN_ERR_INVALID_ARG;
-    if (bad_pages(block_table, max_blocks, page_size, num_pages)) return ATTN_ERR_INVALID_ARG;
-    if (B <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
-    if (h_q % h_kv != 0 || window < 0 || !isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_INVALID_ARG;
-    if (split_tokens < 0 || split_tokens % 64) return ATTN_ERR_INVALID_ARG;
-    if (page_size % 32) return ATTN_ERR_UNSUPPORTED;
-    if (d_h != 128) return ATTN_ERR_UNSUPPORTED;
-    if (B > 65535 || h_kv * ((h_q / h_kv + 15) / 16) > 65535) return ATTN_ERR_UNSUPPORTED;
-    if ((long long)B * max_blocks > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
-    const int S_max = max_blocks * page_size;
-    const int split = resolve_decode_split(split_tokens, B, S_max, h_q, h_kv);
-    const int ns = (S_max + split - 1) / split;
-    const size_t need = attn_decode_workspace_size(B, S_max, h_q, h_kv, d_h, split_tokens);
-    if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-    float *ws_o = static_cast<float *>(workspace);
-    char *ws_end = static_cast<char *>(workspace) + align_up((size_t)B * h_q * ns * d_h * sizeof(float), 256);
-    float *ws_lse = reinterpret_cast<float *>(ws_end);
-    int32_t *plan = reinterpret_cast<int32_t *>(ws_end + align_up((size_t)B * h_q * ns * sizeof(float), 256));
-    mi355::DecodeArgs a{q, k_pages, v_pages, o, lse, seq_lens, B, S_max, h_q, h_kv, d_h,
-                        window, scale, split, ns, ws_o, ws_lse, plan, device_cu_count(),
-                        block_table, max_blocks, page_size, num_pages, sinks};
-    return mi355::launch_decode_bf16_d128(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return decode_paged_launch(q, k_pages, v_pages, nullptr, nullptr, o, lse, seq_lens, block_table,
+                               B, max_blocks, page_size, num_pages, h_q, h_kv, d_h, window, scale,
+                               sinks, split_tokens, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_paged_fp8(const void *q, const void *k_pages, const void *v_pages,
+                                    const float *k_scales, const float *v_scales, void *o,
+                                    float *lse, const int32_t *seq_lens,
+                                    const int32_t *block_table, int B, int max_blocks,
+                                    int page_size, int num_pages, int h_q, int h_kv, int d_h,
+                                    int window, float scale, const float *sinks, int split_tokens,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (bad_ptr(k_scales) || bad_ptr(v_scales)) return ATTN_ERR_INVALID_ARG;
+    return decode_paged_launch(q, k_pages, v_pages, k_scales, v_scales, o, lse, seq_lens,
+                               block_table, B, max_blocks, page_size, num_pages, h_q, h_kv, d_h,
+                               window, scale, sinks, split_tokens, workspace, workspace_bytes,
+                               stream);
+}
+
+attn_status_t attn_quantize_kv_fp8(const void *x, void *codes, float *scales, int B, int h_kv,
+                                   int S, int d_h, hipStream_t stream) {
+    if (bad_ptr(x) || bad_ptr(codes) || bad_ptr(scales)) return ATTN_ERR_INVALID_ARG;
+    if (B <= 0 || h_kv <= 0 || S <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
+    if (d_h % 8) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * h_kv * S * d_h >= (1LL << 40)) return ATTN_ERR_UNSUPPORTED;
+    return mi355::launch_quantize_kv_fp8(x, codes, scales, (long long)B * h_kv, S, d_h, stream) ==
+                   hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 size_t mla_decode_workspace_size(int B, int S_max, int h_q, int d_c, int d_r, int split_tokens) {

@@ -1,6 +1,6 @@
-// decode_bf16.hip -- single-token GQA decode against a bf16 KV cache (d_h = 128),
-// split over the cache ("flash-decoding"), plus the log-sum-exp merge of the
-// split partials shared with the MLA decode.
+// decode_bf16.hip -- single-token GQA decode against a bf16 or FP8 (E4M3) KV
+// cache (d_h = 128), split over the cache ("flash-decoding"), plus the
+// log-sum-exp merge of the split partials shared with the MLA decode.
 //
 // Method: the one new query of each sequence attends to every cached key of
 // that sequence ("Attention deep dive (MHA -> MQA -> GQA -> FlashAttention)",
@@ -62,9 +62,42 @@ constexpr int LDS_BYTES = NW * (WAVE_BYTES + QBUF_BYTES);
 static_assert(LDS_BYTES <= 160 * 1024, "decode rings exceed the LDS");
 static_assert(NSTG >= 2 && NSTG <= 4, "the wait below handles up to 3 tiles in flight");
 constexpr float TAU = 8.0f;
+// FP8 cache: K and V rows of 128 one-byte codes stored 144 bytes apart (9
+// 16-byte slots): the 8-byte row reads of 16 consecutive rows and the 8-bit
+// transposing reads of 16 rows x 16 bytes both hit 64 distinct banks.
+constexpr int ROW8 = D + 16;              // 144 B
+constexpr int KREG8 = 5 * 1024;           // K rows (4608 B) padded to whole one-KB blocks
+constexpr int STAGE_BLK8 = 10;            // K and V regions of an FP8 stage
+static_assert(BN * ROW8 <= KREG8 && KREG8 + BN * ROW8 <= STAGE_BLK8 * 1024, "FP8 stage layout");
+#ifndef DECODE8_NSTG
+#define DECODE8_NSTG 2
+#endif
+#ifndef DECODE8_NW
+#define DECODE8_NW 6
+#endif
+// An FP8 stage is 10 KB instead of 18, so the FP8 kernel runs six waves per
+// workgroup (measured at the 70B workload: 0.418 ms against 0.437 ms with
+// four; a third ring stage with four waves gave nothing).
+template <bool FP8> struct Layout {
+    static constexpr int nstg = FP8 ? DECODE8_NSTG : NSTG;
+    static constexpr int nw = FP8 ? DECODE8_NW : NW;
+    static constexpr int blk = FP8 ? STAGE_BLK8 : STAGE_BLK;      // one-KB copy blocks per stage
+    static constexpr int bytes = blk * 1024;
+    static constexpr int wave = nstg * bytes;
+    static constexpr int lds = nw * (wave + QBUF_BYTES);
+    static constexpr int kreg = FP8 ? KREG8 : KREG;
+    static constexpr int krow = FP8 ? ROW8 : KROW;
+    static constexpr int vrow = FP8 ? ROW8 : VROW;
+    static constexpr int row_bytes = FP8 ? D : 2 * D;              // one cache row in HBM
+};
 
 struct Params {
-    const __bf16 *q, *k, *v;
+    const __bf16 *q;
+    const char *k, *v;                    // bf16 rows or FP8 (E4M3) codes
+    // FP8: one scale per 32 positions of a K/V head: contiguous
+    // [B, h_kv, n_stiles], paged [num_pages, h_kv, page_size / 32]
+    const float *k_scales, *v_scales;
+    int n_stiles;
     const int32_t *seq_lens;
     // paged cache: k and v are [num_pages, h_kv, page_size, D]; position t of
     // sequence b is row t % page_size of page block_table[b * max_blocks +
@@ -118,8 +151,26 @@ struct Unit {
 // PAGED: the tiles of a chunk start on 32-key boundaries, so that a tile
 // never straddles two pages (page sizes are multiples of 32); keys before
 // the visible start of the first tile are masked.
-template <bool PAGED>
-__global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) {
+// FP8: the cache holds E4M3 codes with one scale per 32-position tile of a
+// head (tiles aligned as for PAGED, so each tile has one K and one V scale).
+// A tile is copied to LDS as codes (half the bytes), the codes are widened
+// to bf16 in registers (exact) as they are read for the MFMAs, the K scale
+// multiplies the tile's scores and the V scale its probabilities in the P.V
+// operand (the running sum l takes the unscaled probabilities).
+template <bool PAGED, bool FP8>
+__global__ __launch_bounds__(64 * Layout<FP8>::nw, 1) void decode_bf16_d128_kernel(Params p) {
+    using LY = Layout<FP8>;
+    constexpr int NSTG = LY::nstg;
+    constexpr int NW = LY::nw;
+    static_assert(LY::lds <= 160 * 1024 && NSTG >= 2 && NSTG <= 3, "decode ring");
+    constexpr bool ALIGN = PAGED || FP8;
+    constexpr int STAGE_BLK = LY::blk;
+    constexpr int STAGE_BYTES = LY::bytes;
+    constexpr int WAVE_BYTES = LY::wave;
+    constexpr int KREG = LY::kreg;
+    constexpr int KROW = LY::krow;
+    constexpr int VROW = LY::vrow;
+    constexpr int RB = LY::row_bytes;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -136,7 +187,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
     // each wait below lets exactly the instructions issued after the one
     // waited for stay in flight (vmcnt drains in issue order).
     int vmc = 0;
-    auto wait_after = [&](int mark) { wait_vmcnt_dyn(min(vmc - mark, 31)); };   // fewer is stricter
+    auto wait_after = [&](int mark) { wait_vmcnt_dyn(min(vmc - mark, 63)); };   // fewer is stricter
 
     // Unit id -> geometry.  Each cursor visits increasing unit ids, so its
     // sequence index is found by walking forward from its previous one.
@@ -163,15 +214,15 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         const int kvis = p.window > 0 ? max(0, len - p.window) : 0;
         d.lo = max(d.c * p.split, kvis);
         d.hi = min((d.c + 1) * p.split, len);
-        d.t_first = PAGED ? (d.lo & ~(BN - 1)) : d.lo;
+        d.t_first = ALIGN ? (d.lo & ~(BN - 1)) : d.lo;
         d.n_tiles = d.lo < d.hi ? (d.hi - d.t_first + BN - 1) / BN : 0;
         return d;
     };
 
     // Per-lane DMA offsets inside a tile: block i of a stage covers stage
     // bytes [1024 i, 1024 i + 1024); lane byte o = 1024 i + 16 lane holds K row
-    // o / 272 (o < 9216; rows past 31 and pad slots take a valid chunk of the
-    // last row) or V row (o - 9216) / 288, chunk (remainder) / 16.
+    // o / KROW (o < KREG; rows past 31 and pad slots take a valid chunk of the
+    // last row) or V row (o - KREG) / VROW, chunk (remainder) / 16.
     // The byte offset of each block's lane chunk relative to the tile's
     // first K (or V) row is fixed; only the ragged last tile of a unit needs
     // its rows clamped.
@@ -183,8 +234,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         const bool is_v = i * 1024 >= KREG;         // wave-uniform: blocks never straddle K and V
         const int ro = is_v ? o - KREG : o;
         const int r = min(is_v ? ro / VROW : ro / KROW, BN - 1);
-        const int col = min((ro - r * (is_v ? VROW : KROW)) >> 4, D / 8 - 1) * 16;
-        blk_off[i] = (uint32_t)(r * D * 2 + col);
+        const int col = min((ro - r * (is_v ? VROW : KROW)) >> 4, RB / 16 - 1) * 16;
+        blk_off[i] = (uint32_t)(r * RB + col);
         is_v_mask |= (unsigned)is_v << i;
     }
     const uint32_t ring_lds = lds_offset(ring);
@@ -192,12 +243,13 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
     // Fetch cursor: unit id fu (geometry fd), tile ft; fetched-tile counter nf;
     // vm_tile[s] = value of vmc once the tile in ring stage s was issued.
     int fu = wid, ft = 0, nf = 0, f_walk = 0;
-    // With two stages at most two fetched tiles are unconsumed: vm_last /
-    // vm_prev hold vmc after the issue of tile nf-1 / nf-2 (plain scalars: an
-    // indexed array would live in scratch memory, whose accesses are
-    // vector-memory instructions too).
-    static_assert(NSTG == 2, "the issue bookkeeping below tracks two stages");
-    int vm_last = 0, vm_prev = 0;
+    // At most NSTG (2 or 3) fetched tiles are unconsumed: vm_last / vm_prev /
+    // vm_prev2 hold vmc after the issue of tile nf-1 / nf-2 / nf-3 (plain
+    // scalars: an indexed array would live in scratch memory, whose accesses
+    // are vector-memory instructions too).
+    int vm_last = 0, vm_prev = 0, vm_prev2 = 0;
+    // FP8: scale index of the tile in each ring stage
+    long long sidx0 = 0, sidx1 = 0, sidx2 = 0;
     Unit fd;
     if (fu < total) fd = describe(fu, f_walk);
     auto fetch_skip_empty = [&]() {
@@ -211,18 +263,28 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
         fetch_skip_empty();
         if (fu >= total) return false;
         const int t0 = fd.t_first + ft * BN;
-        size_t row0;                             // element offset of the tile's first row
+        size_t row0;                             // index of the tile's first row
+        long long sidx = 0;
         if constexpr (PAGED) {
             int pg = ld_uniform(p.block_table, fd.b * p.max_blocks + t0 / p.page_size);
             pg = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
-            row0 = (((size_t)pg * p.hkv + fd.g) * p.page_size + (t0 % p.page_size)) * D;
+            row0 = ((size_t)pg * p.hkv + fd.g) * p.page_size + (t0 % p.page_size);
+            sidx = ((long long)pg * p.hkv + fd.g) * (p.page_size / BN) + (t0 % p.page_size) / BN;
         } else {
-            row0 = (((size_t)fd.b * p.hkv + fd.g) * (size_t)p.S_max + t0) * D;
+            row0 = ((size_t)fd.b * p.hkv + fd.g) * (size_t)p.S_max + t0;
+            sidx = ((long long)fd.b * p.hkv + fd.g) * p.n_stiles + t0 / BN;
         }
-        const char *kg = reinterpret_cast<const char *>(p.k + row0);
-        const char *vg = reinterpret_cast<const char *>(p.v + row0);
+        if constexpr (FP8) {                     // branch-free: the stage is wave-uniform
+            const int stg = nf % NSTG;
+            sidx0 = stg == 0 ? sidx : sidx0;
+            sidx1 = stg == 1 ? sidx : sidx1;
+            sidx2 = stg == 2 ? sidx : sidx2;
+        }
+        const char *kg = p.k + row0 * RB;
+        const char *vg = p.v + row0 * RB;
         const uint32_t stage = ring_lds + (nf % NSTG) * STAGE_BYTES;
         vmc += STAGE_BLK;
+        vm_prev2 = vm_prev;
         vm_prev = vm_last;
         vm_last = vmc;
         if (t0 + BN <= fd.hi) {
@@ -230,11 +292,11 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
             for (int i = 0; i < STAGE_BLK; ++i)
                 dma16_off_at<true>(((is_v_mask >> i) & 1) ? vg : kg, blk_off[i], stage + i * 1024);
         } else {                                   // ragged tile: rows past the end re-read the last row
-            const uint32_t lim = (uint32_t)(fd.hi - 1 - t0) * (D * 2);
+            const uint32_t lim = (uint32_t)(fd.hi - 1 - t0) * RB;
 #pragma unroll
             for (int i = 0; i < STAGE_BLK; ++i) {
-                const uint32_t row_b = blk_off[i] & ~(uint32_t)(D * 2 - 1);
-                const uint32_t off = row_b > lim ? lim + (blk_off[i] & (D * 2 - 1)) : blk_off[i];
+                const uint32_t row_b = blk_off[i] & ~(uint32_t)(RB - 1);
+                const uint32_t off = row_b > lim ? lim + (blk_off[i] & (RB - 1)) : blk_off[i];
                 dma16_off_at<true>(((is_v_mask >> i) & 1) ? vg : kg, off, stage + i * 1024);
             }
         }
@@ -245,8 +307,15 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
 
     // V^T operand: lane j of group q16 addresses V row 4 q16 + j/4 (second
     // read: +16), d = 16 db + 4 (j%4) .. +3: chunk 2 db + (j%4)/2, byte 8 (j%2).
-    const int v_lane_off = KREG + (4 * q16 + (j16 >> 2)) * VROW + ((j16 & 3) >> 1) * 16 + 8 * (j16 & 1);
-    const int k_lane_off = j16 * KROW + q16 * 16;
+    // FP8: the transposing 8-bit read gives lane j16 column j16 of the 8 rows
+    // addressed by its group's lane pairs; pair r addresses key
+    // 16 (r / 4) + 4 q16 + r % 4 -- the key order of the probability operand
+    // (the score accumulator's element order) -- bytes 8 (j16 % 2) .. +7 of a
+    // 16-column block.  K codes: 8 bytes of row j16 (+16) at d = 8 q16 + 32 ks.
+    const int v_lane_off = FP8
+        ? KREG + (16 * ((j16 >> 1) >> 2) + 4 * q16 + ((j16 >> 1) & 3)) * VROW + 8 * (j16 & 1)
+        : KREG + (4 * q16 + (j16 >> 2)) * VROW + ((j16 & 3) >> 1) * 16 + 8 * (j16 & 1);
+    const int k_lane_off = FP8 ? j16 * KROW + q16 * 8 : j16 * KROW + q16 * 16;
 
     // Query rows of a unit: 16 heads x 256 B, contiguous in q, copied into the
     // wave's query buffer (4 one-KB blocks; rows past the group's heads
@@ -299,20 +368,40 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
 
         for (int j = 0; j < d.n_tiles; ++j) {
             // this tile is the nc_done-th fetched; a later one may be in flight
-            wait_after(nc_done == nf - 1 ? vm_last : vm_prev);   // this tile's copies landed
+            float k_sc = 1.f, v_sc = 1.f;
+            if constexpr (FP8) {                      // scalar loads, in flight during the wait
+                const int stg = nc_done % NSTG;
+                const long long si = stg == 0 ? sidx0 : (stg == 1 ? sidx1 : sidx2);
+                k_sc = ld_uniform_f(p.k_scales, si);
+                v_sc = ld_uniform_f(p.v_scales, si);
+            }
+            // this tile's copies landed (later tiles may still be in flight)
+            wait_after(nc_done == nf - 1 ? vm_last : (nc_done == nf - 2 ? vm_prev : vm_prev2));
             const char *st = ring + (nc_done % NSTG) * STAGE_BYTES;
             const int t0 = d.t_first + j * BN;
             bf16x8 ka[2][4];
+            bf16x8 vop[8];
+            if constexpr (FP8) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+                for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    ka[mb][ks] = *reinterpret_cast<const bf16x8 *>(st + k_lane_off + 16 * mb * KROW + 64 * ks);
-            bf16x4 va[8][2];
+                    for (int ks = 0; ks < 4; ++ks)
+                        ka[mb][ks] = fp8x8_to_bf16x8(
+                            *reinterpret_cast<const i32x2 *>(st + k_lane_off + 16 * mb * KROW + 32 * ks));
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                va[db][0] = lds_read_tr16(st + v_lane_off + 32 * db);
-                va[db][1] = lds_read_tr16(st + v_lane_off + 16 * VROW + 32 * db);
+                for (int db = 0; db < 8; ++db) vop[db] = fp8x8_to_bf16x8(lds_read_tr8(st + v_lane_off + 16 * db));
+            } else {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        ka[mb][ks] = *reinterpret_cast<const bf16x8 *>(st + k_lane_off + 16 * mb * KROW + 64 * ks);
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const bf16x4 v0 = lds_read_tr16(st + v_lane_off + 32 * db);
+                    const bf16x4 v1 = lds_read_tr16(st + v_lane_off + 16 * VROW + 32 * db);
+                    vop[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
             }
             f32x4 sacc[2];
 #pragma unroll
@@ -323,16 +412,17 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
                     sacc[mb] = mfma16x16x32(ka[mb][ks], qop[ks], sacc[mb]);
                 }
             // element (mb, i) of this lane is key t0 + 16 mb + 4 q16 + i of head column j16
-            const bool tail = t0 + BN > d.hi || (PAGED && t0 < d.lo);
+            const bool tail = t0 + BN > d.hi || (ALIGN && t0 < d.lo);
+            const float sl = FP8 ? p.scale_log2 * k_sc : p.scale_log2;
             float x[8];
             float mx = -INFINITY;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float v = sacc[mb][i] * p.scale_log2;
+                    float v = sacc[mb][i] * sl;
                     const int key = t0 + 16 * mb + 4 * q16 + i;
-                    if (tail) v = (key < d.hi && (!PAGED || key >= d.lo)) ? v : -INFINITY;
+                    if (tail) v = (key < d.hi && (!ALIGN || key >= d.lo)) ? v : -INFINITY;
                     x[4 * mb + i] = v;
                     mx = fmaxf(mx, v);
                 }
@@ -355,12 +445,13 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_bf16_d128_kernel(Params p) 
                 lsum += pv[e];
             }
             l_run = l_run * alpha + lsum;
+            if constexpr (FP8) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] *= v_sc;
+            }
             const bf16x8 pop = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const bf16x8 a = __builtin_shufflevector(va[db][0], va[db][1], 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[db] = mfma16x16x32(a, pop, oacc[db]);
-            }
+            for (int db = 0; db < 8; ++db) oacc[db] = mfma16x16x32(vop[db], pop, oacc[db]);
             ++nc_done;
             // refill the consumed stage once every read of it has returned
             asm volatile("" ::: "memory");
@@ -478,8 +569,11 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float *ws_o, c
 hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
     Params p;
     p.q = static_cast<const __bf16 *>(a.q);
-    p.k = static_cast<const __bf16 *>(a.k_cache);
-    p.v = static_cast<const __bf16 *>(a.v_cache);
+    p.k = static_cast<const char *>(a.k_cache);
+    p.v = static_cast<const char *>(a.v_cache);
+    p.k_scales = a.k_scales;
+    p.v_scales = a.v_scales;
+    p.n_stiles = (a.S_max + BN - 1) / BN;
     p.seq_lens = a.seq_lens;
     p.block_table = a.block_table;
     p.max_blocks = a.max_blocks;
@@ -504,26 +598,36 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     static bool attr_set = false;
     if (!attr_set) {
-        e = hipFuncSetAttribute((const void *)decode_bf16_d128_kernel<false>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute((const void *)decode_bf16_d128_kernel<true>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
+        const void *fns[4] = {(const void *)decode_bf16_d128_kernel<false, false>,
+                              (const void *)decode_bf16_d128_kernel<true, false>,
+                              (const void *)decode_bf16_d128_kernel<false, true>,
+                              (const void *)decode_bf16_d128_kernel<true, true>};
+        const int lds[4] = {Layout<false>::lds, Layout<false>::lds, Layout<true>::lds, Layout<true>::lds};
+        for (int i = 0; i < 4; ++i) {
+            e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds[i]);
+            if (e != hipSuccess) return e;
+        }
         attr_set = true;
     }
     // persistent grid: one workgroup per CU (its LDS takes most of the CU),
     // never more workgroups than the largest possible number of units needs
     const long long max_units = (long long)a.B * a.hkv * p.n_hchunk * a.n_split_max;
-    long long blocks = (max_units + NW - 1) / NW;
+    const int nw = a.k_scales ? Layout<true>::nw : Layout<false>::nw;
+    long long blocks = (max_units + nw - 1) / nw;
     if (blocks > a.num_cus) blocks = a.num_cus;
     if (blocks < 1) blocks = 1;
-    if (a.block_table)
-        hipLaunchKernelGGL(decode_bf16_d128_kernel<true>, dim3((unsigned)blocks), dim3(64 * NW),
-                           LDS_BYTES, stream, p);
-    else
-        hipLaunchKernelGGL(decode_bf16_d128_kernel<false>, dim3((unsigned)blocks), dim3(64 * NW),
-                           LDS_BYTES, stream, p);
+    const dim3 grid((unsigned)blocks), block(64 * nw);
+    if (a.k_scales) {
+        if (a.block_table)
+            hipLaunchKernelGGL((decode_bf16_d128_kernel<true, true>), grid, block, Layout<true>::lds, stream, p);
+        else
+            hipLaunchKernelGGL((decode_bf16_d128_kernel<false, true>), grid, block, Layout<true>::lds, stream, p);
+    } else {
+        if (a.block_table)
+            hipLaunchKernelGGL((decode_bf16_d128_kernel<true, false>), grid, block, Layout<false>::lds, stream, p);
+        else
+            hipLaunchKernelGGL((decode_bf16_d128_kernel<false, false>), grid, block, Layout<false>::lds, stream, p);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_combine(a.ws_o, a.ws_lse, a.seq_lens, a.o, a.lse, a.B, a.hq, D, a.S_max,

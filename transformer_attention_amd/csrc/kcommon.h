@@ -187,7 +187,7 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N & 0x30) << 10) | (0x7 << 4) | (0xF << 8));
 }
-// wait_vmcnt with a wave-uniform runtime count in [0, 31] (larger counts wait
+// wait_vmcnt with a wave-uniform runtime count in [0, 63] (larger counts wait
 // for everything, which is always safe).
 __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
     switch (n) {
@@ -222,6 +222,38 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
         case 29: wait_vmcnt<29>(); break;
         case 30: wait_vmcnt<30>(); break;
         case 31: wait_vmcnt<31>(); break;
+        case 32: wait_vmcnt<32>(); break;
+        case 33: wait_vmcnt<33>(); break;
+        case 34: wait_vmcnt<34>(); break;
+        case 35: wait_vmcnt<35>(); break;
+        case 36: wait_vmcnt<36>(); break;
+        case 37: wait_vmcnt<37>(); break;
+        case 38: wait_vmcnt<38>(); break;
+        case 39: wait_vmcnt<39>(); break;
+        case 40: wait_vmcnt<40>(); break;
+        case 41: wait_vmcnt<41>(); break;
+        case 42: wait_vmcnt<42>(); break;
+        case 43: wait_vmcnt<43>(); break;
+        case 44: wait_vmcnt<44>(); break;
+        case 45: wait_vmcnt<45>(); break;
+        case 46: wait_vmcnt<46>(); break;
+        case 47: wait_vmcnt<47>(); break;
+        case 48: wait_vmcnt<48>(); break;
+        case 49: wait_vmcnt<49>(); break;
+        case 50: wait_vmcnt<50>(); break;
+        case 51: wait_vmcnt<51>(); break;
+        case 52: wait_vmcnt<52>(); break;
+        case 53: wait_vmcnt<53>(); break;
+        case 54: wait_vmcnt<54>(); break;
+        case 55: wait_vmcnt<55>(); break;
+        case 56: wait_vmcnt<56>(); break;
+        case 57: wait_vmcnt<57>(); break;
+        case 58: wait_vmcnt<58>(); break;
+        case 59: wait_vmcnt<59>(); break;
+        case 60: wait_vmcnt<60>(); break;
+        case 61: wait_vmcnt<61>(); break;
+        case 62: wait_vmcnt<62>(); break;
+        case 63: wait_vmcnt<63>(); break;
         default: wait_vmcnt<0>(); break;
     }
 }
@@ -311,6 +343,30 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 __device__ __forceinline__ bf16x4 lds_read_tr16(const void *lds_ptr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
         (lds_bf16x4_t *)((__attribute__((address_space(3))) char *)lds_ptr));
+}
+
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+// ds_read_b64_tr_b8: within each 16-lane group, result lane i byte r is byte
+// i % 8 of the 8 bytes addressed by lane 2r + i / 8 of that group (so if lanes
+// 2r and 2r+1 address the two halves of 16 bytes of row r, lane i receives
+// column i of the group's 8 rows).
+__device__ __forceinline__ i32x2 lds_read_tr8(const void *lds_ptr) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (lds_i32x2_t *)((__attribute__((address_space(3))) char *)lds_ptr));
+}
+// Eight OCP FP8 E4M3 codes (byte r of the pair of words = element r) to bf16.
+// Every E4M3 value is exact in bf16 (3 mantissa bits, exponents in range).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(i32x2 w) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+__device__ __forceinline__ float ld_uniform_f(const float *p, long long i) {
+    return ((const __attribute__((address_space(4))) float *)p)[i];
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {

@@ -58,6 +58,10 @@ struct DecodeArgs {
     const int32_t *block_table;
     int max_blocks, page_size, num_pages;
     const float *sinks;   // [hq] sink logits or nullptr
+    // FP8 (E4M3) cache when non-null: k_cache / v_cache hold one-byte codes
+    // and these one scale per 32 positions of a K/V head ([B, hkv,
+    // ceil(S_max / 32)] contiguous, [num_pages, hkv, page_size / 32] paged)
+    const float *k_scales, *v_scales;
 };
 hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream);
 
@@ -83,6 +87,10 @@ hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream);
 // Merge of split partials: o[b,h,:] (bf16) and lse[b,h] (natural log, may be
 // null) from ws_o/ws_lse over the ceil(len_b / split) splits of sequence b;
 // sinks (per head, may be null) adds a sink logit to each merged denominator.
+// Per-tile FP8 (E4M3) quantisation of a bf16 cache x [B*hkv, S, d]: one
+// scale per 32 positions of a head (amax / 448), codes [B*hkv, S, d].
+hipError_t launch_quantize_kv_fp8(const void *x, void *codes, float *scales, long long n_heads,
+                                  int S, int d, hipStream_t stream);
 hipError_t launch_split_combine(const float *ws_o, const float *ws_lse,
                                 const int32_t *seq_lens, void *o, float *lse,
                                 int B, int H, int dv, int S_max, int split,

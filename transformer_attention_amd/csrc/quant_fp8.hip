@@ -1,0 +1,73 @@
+// quant_fp8.hip -- per-tile FP8 (OCP E4M3) quantisation of a bf16 KV cache.
+//
+// The pages quantise each tile with the scale amax / 448, 448 being the
+// largest E4M3 value, and cast x / scale to E4M3 ("Flash Attention 3 and
+// Multi-Headed Latent Attention", the FP8 attention section); a quantised
+// KV cache halves the cache bytes ("Attention deep dive (MHA -> MQA -> GQA ->
+// FlashAttention)", section 5, production-engine notes).  Here a tile is 32
+// consecutive positions of one K/V head (all d values), the tile the decode
+// kernel streams, so each streamed tile carries one scale.  An all-zero tile
+// gets scale 1.  The division is IEEE fp32 and the cast rounds to nearest
+// even (v_cvt_pk_fp8_f32), with magnitudes clamped to 448 first.
+//
+// One wave per tile: a pass for the absolute maximum, then a pass that
+// writes the codes (the second reads the tile again, mostly from L2).  It is
+// bound by HBM: 2 bytes read and 1 written per value.
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace mi355 {
+namespace {
+
+constexpr int TILE = 32;
+
+__global__ __launch_bounds__(256) void quantize_kv_fp8_kernel(const __bf16 *x, uint8_t *codes,
+                                                              float *scales, long long n_tiles,
+                                                              int nt, int S, int d) {
+    const long long tile = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (tile >= n_tiles) return;
+    const int lane = threadIdx.x & 63;
+    const long long head = tile / nt;
+    const int t = (int)(tile - head * nt);
+    const int r0 = t * TILE;
+    const int r1 = min(r0 + TILE, S);
+    const size_t base = ((size_t)head * S + r0) * d;
+    const int n = (r1 - r0) * d;                      // a multiple of 8
+    float amax = 0.f;
+    for (int c = 8 * lane; c < n; c += 512) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, ldg16(x + base + c));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (lane == 0) scales[tile] = sc;
+    for (int c = 8 * lane; c < n; c += 512) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, ldg16(x + base + c));
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf((float)v[e] / sc, -448.0f), 448.0f);
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+        *reinterpret_cast<i32x2 *>(codes + base + c) = i32x2{w0, w1};
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_kv_fp8(const void *x, void *codes, float *scales, long long n_heads,
+                                  int S, int d, hipStream_t stream) {
+    const int nt = (S + TILE - 1) / TILE;
+    const long long n_tiles = n_heads * nt;
+    const long long blocks = (n_tiles + 3) / 4;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quantize_kv_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const __bf16 *>(x), static_cast<uint8_t *>(codes), scales,
+                       n_tiles, nt, S, d);
+    return hipGetLastError();
+}
+
+}  // namespace mi355

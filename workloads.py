@@ -119,6 +119,22 @@ def prefill_inputs(shape: PrefillShape, *, seed: int = 0, device="cpu",
     return q.to(device), k.to(device), v.to(device)
 
 
+def random_fp8_cache(shape, *, seed: int, device="cpu", tile: int = 32):
+    """A synthetic FP8 (E4M3) cache: random one-byte codes of both signs with
+    exponent fields 3..10 and any mantissa (so never the NaN code), and one
+    random power-of-two scale per `tile` positions, 2^-8 .. 2^-5.  The
+    dequantised values then span about 2^-12 .. 2^-1.  shape = [..., S, d];
+    generated on `device`; returns (codes uint8, scales float32
+    [..., ceil(S / tile)])."""
+    g = _gen(seed, device)
+    r = torch.randint(0, 256, shape, generator=g, dtype=torch.uint8, device=device)
+    codes = (r & 0x87) | ((((r >> 3) & 7) + 3) << 3)
+    nt = (shape[-2] + tile - 1) // tile
+    e = torch.randint(-8, -4, tuple(shape[:-2]) + (nt,), generator=g, dtype=torch.int32, device=device)
+    scales = torch.pow(2.0, e.to(torch.float32))
+    return codes, scales
+
+
 def seq_lengths(B: int, lo: int, hi: int, *, seed: int) -> torch.Tensor:
     """Per-sequence cache lengths, uniform on the integers [lo, hi]."""
     g = _gen(seed, "cpu")
