@@ -79,6 +79,8 @@ def _load():
     lib.oracle_quantize_kv_fp8.restype = I
     lib.oracle_decode_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, P]
     lib.oracle_decode_fp8.restype = I
+    lib.oracle_rope.argtypes = [P, P, P, I, I, I, I, I, I, D]
+    lib.oracle_rope.restype = I
     lib.oracle_merge_partials.argtypes = [P, P, I, I, P, P]
     lib.oracle_merge_partials.restype = None
     lib.oracle_set_threads.argtypes = [I]
@@ -328,6 +330,24 @@ def decode_paged_fp8(q, k8_pages, v8_pages, k_scale_pages, v_scale_pages, block_
     vs = gather_pages(_f32(v_scale_pages)[..., None], block_table, lens_t, head_axis=True)[..., 0]
     assert ks.shape[2] * 32 == k8.shape[2] and ps % 32 == 0
     return decode_fp8(q, k8, v8, ks, vs, lens, window=window, scale=scale, sinks=sinks)
+
+
+def rope(x, *, positions=None, base: float, rope_offset: int = 0, rope_dim=None):
+    """Rotary position embedding of x:[B, H, T, row] (dimensions [rope_offset,
+    rope_offset + rope_dim) in interleaved pairs, theta_j = base^(-2j/rope_dim),
+    angle = position * theta_j); positions:[B, T] ints, default t.  float64."""
+    x = _f32(x)
+    B, H, T, row = x.shape
+    rd = row - rope_offset if rope_dim is None else rope_dim
+    out = np.zeros(x.shape, dtype=np.float64)
+    pos = None if positions is None else np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    if pos is not None:
+        assert pos.shape == (B, T)
+    rc = _load().oracle_rope(_ptr(x), None if pos is None else _ptr(pos), _ptr(out), B, H, T, row,
+                             int(rope_offset), int(rd), float(base))
+    if rc != 0:
+        raise ValueError("oracle_rope: invalid arguments")
+    return out
 
 
 def merge_partials(parts_o, parts_lse):

@@ -579,3 +579,42 @@ int oracle_decode_fp8(const float *q, const unsigned char *k8, const unsigned ch
     }
     return 0;
 }
+
+/*
+ * Rotary position embedding ("Attention Engineering: From MHA to GQA, MLA &
+ * FlashAttention", section 1, the complex-plane derivation and the
+ * relative-distance identity): the rotated dimensions of a row are taken in
+ * pairs (x_{2j}, x_{2j+1}), j = 0 .. rope_dim/2 - 1, each a complex number
+ * rotated by the angle m * theta_j at token position m, with
+ * theta_j = base^(-2j / rope_dim):
+ *   x'_{2j}   = x_{2j} cos(m theta_j) - x_{2j+1} sin(m theta_j)
+ *   x'_{2j+1} = x_{2j} sin(m theta_j) + x_{2j+1} cos(m theta_j).
+ * The rotated dimensions are [rope_offset, rope_offset + rope_dim) of each
+ * row (the whole head for GQA; the decoupled 64-d tail for MLA); the others
+ * are copied.  x:[B, H, T, row] float; positions: [B, T] int or NULL (then
+ * m = t); out:[B, H, T, row] double.
+ */
+int oracle_rope(const float *x, const int *positions, double *out, int B, int H, int T,
+                int row, int rope_offset, int rope_dim, double base)
+{
+    if (B < 0 || H < 0 || T < 0 || row <= 0 || rope_dim < 0 || rope_dim % 2 ||
+        rope_offset < 0 || rope_offset + rope_dim > row || !(base > 0.0)) return -1;
+    const long rows = (long)B * H * T;
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r) {
+        const long t = r % T, b = r / ((long)H * T);
+        const double m = positions ? (double)positions[b * T + t] : (double)t;
+        const float *xr = x + r * row;
+        double *orow = out + r * row;
+        for (int e = 0; e < row; ++e) orow[e] = (double)xr[e];
+        for (int j = 0; j < rope_dim / 2; ++j) {
+            const double theta = pow(base, -2.0 * j / rope_dim);
+            const double c = cos(m * theta), s = sin(m * theta);
+            const double a = xr[rope_offset + 2 * j], bb = xr[rope_offset + 2 * j + 1];
+            orow[rope_offset + 2 * j] = a * c - bb * s;
+            orow[rope_offset + 2 * j + 1] = a * s + bb * c;
+        }
+    }
+    return 0;
+}
+
