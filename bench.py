@@ -21,7 +21,7 @@ two device synchronisations; kernel durations come from HIP events recorded
 on the stream the kernels run on.  One JSON line is printed.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|backward|decode|decode-paged|decode-fp8|mla|swa-mha|
+                    [--only prefill|backward|decode|decode-paged|decode-fp8|rope|mla|swa-mha|
                             swa-mqa|copy]
 
 ``--only copy`` times a plain 1 GiB device copy instead: it is the
@@ -187,6 +187,20 @@ def bench_decode_fp8(torch, ta, W, steps, warmup):
             "frac_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
+def bench_rope(torch, ta, W, steps, warmup):
+    """RoPE of the Llama-3-8B prefill's q and k in place (base 5e5): every
+    value read and written once."""
+    s = W.LLAMA3_8B_PREFILL
+    q, k, v = W.prefill_inputs(s, seed=0, device="cuda", gen_device="cuda")
+    del v
+    stream = torch.cuda.current_stream()
+    ms, wall = _events_time(torch, lambda: ta.attn_rope_qk(q, k, base=5e5), steps, warmup, stream)
+    nbytes = 2 * (q.numel() + k.numel()) * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del q, k
+    return {"ms": ms, "wall_s": wall, "bytes": nbytes, "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+
+
 def bench_copy(torch, steps, warmup, nbytes=1 << 30):
     """A plain device-to-device copy of known size (reads and writes nbytes
     each).  Not part of the attention path: its HBM counter readings give the
@@ -266,7 +280,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    choices=["prefill", "backward", "decode", "decode-paged", "decode-fp8", "mla",
+                    choices=["prefill", "backward", "decode", "decode-paged", "decode-fp8", "rope", "mla",
                              "swa-mha",
                              "swa-mqa", "copy"])
     args = ap.parse_args(argv)
@@ -310,6 +324,10 @@ def main(argv=None):
         out["decode_fp8"] = bench_decode_fp8(torch, ta, W, args.steps, args.warmup)
         print(f"[bench] decode (fp8 cache) {out['decode_fp8']['ms']:.3f} ms "
               f"{out['decode_fp8']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    if only in (None, "rope"):
+        out["rope"] = bench_rope(torch, ta, W, args.steps, args.warmup)
+        print(f"[bench] rope (q and k) {out['rope']['ms']:.3f} ms {out['rope']['gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
     if only in (None, "decode-paged"):
         out["decode_paged"] = bench_decode_paged(torch, ta, W, args.steps, args.warmup)
         print(f"[bench] decode (paged) {out['decode_paged']['ms']:.3f} ms "
@@ -378,6 +396,12 @@ def main(argv=None):
                               "frac_hbm_peak": round(d["frac_hbm_peak"], 4), "bytes": d["bytes"]}
         if "decode" in out:
             line["decode_fp8"]["speedup_vs_bf16_cache"] = round(out["decode"]["ms"] / d["ms"], 3)
+    if "rope" in out and next(iter(out)) != "rope":
+        d = out["rope"]
+        line["rope"] = {"workload": "RoPE of the Llama-3-8B prefill's q and k in place (32/8 heads, "
+                                    "T=8192, base 5e5)",
+                        "ms": round(d["ms"], 4), "GB_s": round(d["gbs"], 1),
+                        "frac_hbm_peak": round(d["frac_hbm_peak"], 4), "bytes": d["bytes"]}
     if "backward" in out and next(iter(out)) != "backward":
         r = out["backward"]
         line["backward"] = {"workload": "Llama-3-8B-shaped causal GQA prefill backward (dQ, dK, dV)",

@@ -300,6 +300,30 @@ attn_status_t attn_decode_paged_fp8(const void *q, const void *k_pages, const vo
                                     int split_tokens, void *workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/*
+ * attn_rope_qk -- rotary position embedding of the queries and keys, in
+ * place, in one launch ("Attention Engineering ...", section 1: pair j of
+ * the rotated dimensions, (x_{2j}, x_{2j+1}), is rotated as a complex number
+ * by the angle m theta_j at position m, theta_j = base^(-2j / rope_dim), so
+ * that rotated queries and keys interact through their distance only;
+ * section 3: MLA rotates only the decoupled RoPE part).
+ *
+ *   q : [B, h_q, T, row_q]  dtype  (read and written)
+ *   k : [B, h_k, T, row_k]  dtype  (read and written; NULL with h_k = 0)
+ *   positions : [B, T] int32 device memory, or NULL for positions 0..T-1
+ *               (decode: T = 1 and the new token's position per sequence)
+ * The rotated dimensions of every row are [rope_offset, rope_offset +
+ * rope_dim): rope_offset = 0, rope_dim = d_h for a plain head; 512 and 64
+ * for the MLA query row and the cache row's k_R.  The others are left as
+ * they are.  The angle and its cosine and sine are computed in double
+ * precision, the rotation in fp32, rounded to dtype (bf16: nearest even).
+ * rope_dim and rope_offset must be even, base finite and > 0; dtype
+ * ATTN_BF16 or ATTN_F32.
+ */
+attn_status_t attn_rope_qk(void *q, void *k, const int32_t *positions, int B, int T,
+                           int h_q, int h_k, int row_q, int row_k, int rope_offset,
+                           int rope_dim, float base, attn_dtype_t dtype, hipStream_t stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *attn_status_string(attn_status_t status);
 

@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
               "attn_decode", "mla_decode", "attn_decode_workspace_size",
               "attn_decode_paged", "attn_decode_paged_workspace_size", "mla_decode_paged",
               "mla_decode_paged_workspace_size", "attn_quantize_kv_fp8", "attn_decode_fp8",
-              "attn_decode_paged_fp8",
+              "attn_decode_paged_fp8", "attn_rope_qk",
               "mla_decode_workspace_size", "attn_status_string", "attn_abi_version"):
         assert n in names, n
 
@@ -166,6 +166,22 @@ def test_fp8_validation(lib):
     assert pdec(bt=None) == 1
     assert pdec(ps=48) == 2
     assert pdec(ws=None) == 3
+
+
+def test_rope_validation(lib):
+    def rope(**kw):
+        a = dict(q=FAKE, k=FAKE, pos=None, B=1, T=8, hq=4, hk=2, rq=128, rk=128, off=0, rd=128,
+                 base=1e4, dtype=1)
+        a.update(kw)
+        return lib.attn_rope_qk(a["q"], a["k"], a["pos"], a["B"], a["T"], a["hq"], a["hk"], a["rq"],
+                                a["rk"], a["off"], a["rd"], a["base"], a["dtype"], None)
+    assert rope(q=None) == 1
+    assert rope(k=None) == 1                         # keys announced but missing
+    assert rope(rd=7) == 1                           # odd rotated width
+    assert rope(off=64, rd=128) == 1                 # past the row
+    assert rope(base=0.0) == 1
+    assert rope(base=float("nan")) == 1
+    assert rope(dtype=5) == 2
 
 
 def test_paged_validation(lib):

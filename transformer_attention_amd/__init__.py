@@ -44,7 +44,7 @@ EXPORTED_SYMBOLS = (
     "attn_decode", "attn_decode_workspace_size",
     "mla_decode", "mla_decode_workspace_size", "attn_decode_paged",
     "attn_decode_paged_workspace_size", "mla_decode_paged", "mla_decode_paged_workspace_size",
-    "attn_quantize_kv_fp8", "attn_decode_fp8", "attn_decode_paged_fp8",
+    "attn_quantize_kv_fp8", "attn_decode_fp8", "attn_decode_paged_fp8", "attn_rope_qk",
     "attn_status_string",
     "attn_abi_version",
 )
@@ -100,6 +100,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P,
                                           I, P, Z, P]
     lib.attn_decode_paged_fp8.restype = I
+    lib.attn_rope_qk.argtypes = [P, P, P, I, I, I, I, I, I, I, I, F, I, P]
+    lib.attn_rope_qk.restype = I
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -524,3 +526,31 @@ def attn_decode_paged_fp8(q, k_pages, v_pages, k_scales, v_scales, seq_lens, blo
                                    int(split_tokens), _ptr(workspace), ws_bytes, _stream(q.device))
     _check(st, "attn_decode_paged_fp8")
     return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_rope_qk(q, k=None, *, base: float, positions=None, rope_offset: int = 0, rope_dim=None):
+    """Rotary position embedding, in place: q:[B,h_q,T,row_q] and k:[B,h_k,T,row_k]
+    (bf16 or fp32, same dtype); dimensions [rope_offset, rope_offset + rope_dim)
+    of every row (default: the rest of the row); positions int32[B,T] on the
+    device, default 0..T-1.  Returns (q, k)."""
+    lib = load_library()
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _require(q, "q", q.dtype, ndim=4)
+    B, hq, T, row_q = q.shape
+    hk, row_k = 0, 0
+    if k is not None:
+        _require(k, "k", q.dtype, q.device, 4)
+        if k.shape[0] != B or k.shape[2] != T:
+            raise ValueError("k shape mismatch")
+        hk, row_k = k.shape[1], k.shape[3]
+    if positions is not None:
+        _require(positions, "positions", torch.int32, q.device)
+        if positions.numel() != B * T:
+            raise ValueError("positions must hold [B, T] values")
+    rd = row_q - rope_offset if rope_dim is None else rope_dim
+    st = lib.attn_rope_qk(_ptr(q), _ptr(k), _ptr(positions), B, T, hq, hk, row_q, row_k,
+                          int(rope_offset), int(rd), float(base), _DT[q.dtype], _stream(q.device))
+    _check(st, "attn_rope_qk")
+    return q, k
+

@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG_DIR), "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmi355attn.so")
 SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_bwd_bf16.hip", "prefill_f32.hip",
-           "decode_bf16.hip", "mla_decode_bf16.hip", "quant_fp8.hip"]
+           "decode_bf16.hip", "mla_decode_bf16.hip", "quant_fp8.hip",
+           "rope.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.

@@ -249,6 +249,25 @@ attn_status_t attn_decode_paged_fp8(const void *q, const void *k_pages, const vo
                                stream);
 }
 
+attn_status_t attn_rope_qk(void *q, void *k, const int32_t *positions, int B, int T, int h_q,
+                           int h_k, int row_q, int row_k, int rope_offset, int rope_dim,
+                           float base, attn_dtype_t dtype, hipStream_t stream) {
+    if (bad_ptr(q) || (h_k > 0 && bad_ptr(k))) return ATTN_ERR_INVALID_ARG;
+    if (B <= 0 || T <= 0 || h_q <= 0 || h_k < 0 || row_q <= 0 || (h_k > 0 && row_k <= 0))
+        return ATTN_ERR_INVALID_ARG;
+    if (rope_dim <= 0 || rope_dim % 2 || rope_offset < 0 || rope_offset % 2 ||
+        rope_offset + rope_dim > row_q || (h_k > 0 && rope_offset + rope_dim > row_k))
+        return ATTN_ERR_INVALID_ARG;
+    if (row_q % 2 || (h_k > 0 && row_k % 2)) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(base) || !(base > 0.f)) return ATTN_ERR_INVALID_ARG;
+    if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * h_q * T * row_q >= (1LL << 40) || (long long)B * h_k * T * row_k >= (1LL << 40))
+        return ATTN_ERR_UNSUPPORTED;
+    mi355::RopeArgs a{q, h_k > 0 ? k : nullptr, positions, B, T, h_q, h_k, row_q, row_k,
+                      rope_offset, rope_dim, base, dtype == ATTN_BF16};
+    return mi355::launch_rope_qk(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status_t attn_quantize_kv_fp8(const void *x, void *codes, float *scales, int B, int h_kv,
                                    int S, int d_h, hipStream_t stream) {
     if (bad_ptr(x) || bad_ptr(codes) || bad_ptr(scales)) return ATTN_ERR_INVALID_ARG;

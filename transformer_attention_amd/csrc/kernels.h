@@ -87,6 +87,18 @@ hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream);
 // Merge of split partials: o[b,h,:] (bf16) and lse[b,h] (natural log, may be
 // null) from ws_o/ws_lse over the ceil(len_b / split) splits of sequence b;
 // sinks (per head, may be null) adds a sink logit to each merged denominator.
+// Rotary position embedding of q [B, hq, T, row_q] and k [B, hk, T, row_k]
+// (k may be null with hk = 0), dimensions [rope_offset, rope_offset +
+// rope_dim) of each row, in place.
+struct RopeArgs {
+    void *q, *k;
+    const int32_t *positions;   // [B, T] or nullptr (position t)
+    int B, T, hq, hk, row_q, row_k, rope_offset, rope_dim;
+    float base;
+    bool bf16;
+};
+hipError_t launch_rope_qk(const RopeArgs &a, hipStream_t stream);
+
 // Per-tile FP8 (E4M3) quantisation of a bf16 cache x [B*hkv, S, d]: one
 // scale per 32 positions of a head (amax / 448), codes [B*hkv, S, d].
 hipError_t launch_quantize_kv_fp8(const void *x, void *codes, float *scales, long long n_heads,
