@@ -280,7 +280,10 @@ attn_status_t mla_decode_paged(const void *q, const void *kv_pages, void *o, flo
  * multiplies the scores of its tile and the V scale the weights of its
  * tile's values, accumulation as in attn_decode.  Everything else
  * (arguments, workspace, errors) is as in attn_decode / attn_decode_paged;
- * null k_scales or v_scales is ATTN_ERR_INVALID_ARG.
+ * null k_scales or v_scales is ATTN_ERR_INVALID_ARG.  With split_tokens = 0
+ * the FP8 calls choose longer chunks than the bf16 ones (never shorter), so
+ * attn_decode_workspace_size / attn_decode_paged_workspace_size still cover
+ * them.
  */
 attn_status_t attn_quantize_kv_fp8(const void *x, void *codes, float *scales,
                                    int B, int h_kv, int S, int d_h, hipStream_t stream);
