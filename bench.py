@@ -40,7 +40,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 # rocprofv3 FETCH_SIZE/WRITE_SIZE summaries (KiB per dispatch), scaled by the
 # same counters read on a plain copy kernel of known size; None until taken
 # for the current kernel.
-PREFILL_TRAFFIC_BYTES = 212673444   # prefill_bf16_d128 kernel <1,2,4>: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB
+PREFILL_TRAFFIC_BYTES = 212685895   # prefill_bf16_d128 kernel <1,2,4>: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB
 
 
 def prefill_visible_pairs(T: int, causal: bool, window: int) -> int:
