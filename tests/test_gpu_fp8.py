@@ -95,8 +95,10 @@ def test_decode_fp8_with_sinks_and_empty_sequence(ta, oracle_mod):
     assert torch.all(o[2] == 0)
 
 
-@pytest.mark.parametrize("page_size", [32, 128])
-def test_paged_fp8_equals_contiguous(ta, oracle_mod, page_size):
+@pytest.mark.parametrize("page_size,window", [(32, 0), (128, 0), (64, 100)])
+def test_paged_fp8_equals_contiguous(ta, oracle_mod, page_size, window):
+    """Both FP8 kernels start tiles on 32-key boundaries, so the paged result
+    equals the contiguous one bit for bit, with a window too."""
     B, S_max, hq, hkv = 3, 512, 16, 2
     q, k8, v8, ks, vs, lens = _fp8_case(oracle_mod, B, S_max, hq, hkv, 440 + page_size)
     kc = torch.from_numpy(k8)
@@ -112,16 +114,16 @@ def test_paged_fp8_equals_contiguous(ta, oracle_mod, page_size):
     ksp[perm.cpu()] = torch.from_numpy(ks).view(B, hkv, nb, spp).permute(0, 2, 1, 3).reshape(-1, hkv, spp)
     vsp[perm.cpu()] = torch.from_numpy(vs).view(B, hkv, nb, spp).permute(0, 2, 1, 3).reshape(-1, hkv, spp)
     lens_d = lens.cuda()
-    print(f"[case] paged fp8 ps={page_size}", flush=True)
+    print(f"[case] paged fp8 ps={page_size} w={window}", flush=True)
     o1, l1 = ta.attn_decode_paged_fp8(q.cuda(), kp, vp, ksp.cuda(), vsp.cuda(), lens_d, table,
-                                      return_lse=True)
+                                      window=window, return_lse=True)
     dev = [torch.from_numpy(x).cuda() for x in (k8, v8, ks, vs)]
-    o2, l2 = ta.attn_decode_fp8(q.cuda(), *dev, lens_d, return_lse=True)
+    o2, l2 = ta.attn_decode_fp8(q.cuda(), *dev, lens_d, window=window, return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     ro, rl = oracle_mod.decode_paged_fp8(np32(q), kp.cpu().numpy(), vp.cpu().numpy(), ksp.numpy(),
                                          vsp.numpy(), table.cpu().numpy(), lens.numpy(),
-                                         scale=1 / math.sqrt(128))
+                                         window=window, scale=1 / math.sqrt(128))
     assert_bf16_close(np32(o1)[:, :, 0], ro, "paged fp8")
 
 
