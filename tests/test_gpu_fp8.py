@@ -150,3 +150,19 @@ def test_full_size_fp8_decode(ta, oracle_mod):
                                       vs[b:b + 1, :, :nt].cpu().numpy(), lens[b:b + 1].numpy(),
                                       scale=s.scale)
         assert_bf16_close(np32(o[b:b + 1])[:, :, 0], ro, f"fp8 seq {b}")
+
+
+def test_full_size_quantiser_sampled_tiles(ta, oracle_mod):
+    """The 70B workload's bf16 K cache (64 x 8 heads x 32768 positions x 128)
+    through the GPU quantiser; sampled 32-position tiles against the oracle's
+    quantiser, bit for bit."""
+    s = W.GQA70B_DECODE
+    _, kc, _, _ = W.decode_inputs(s, seed=0, device="cuda", gen_device="cuda")
+    print("[case] full-size quantiser", flush=True)
+    codes, scales = ta.attn_quantize_kv_fp8(kc)
+    torch.cuda.synchronize()
+    for b, g, t in ((0, 0, 0), (17, 3, 511), (63, 7, 1023), (40, 5, 777)):
+        x = np32(kc[b:b + 1, g:g + 1, 32 * t:32 * t + 32])
+        rc, rs = oracle_mod.quantize_kv_fp8(x)
+        assert np.array_equal(codes[b:b + 1, g:g + 1, 32 * t:32 * t + 32].cpu().numpy(), rc)
+        assert scales[b, g, t].item() == float(rs[0, 0, 0])
