@@ -244,3 +244,18 @@ def test_workspace_grows_with_splits(lib):
     a = lib.attn_decode_workspace_size(4, 4096, 16, 2, 128, 64)
     b = lib.attn_decode_workspace_size(4, 4096, 16, 2, 128, 1024)
     assert a > b > 0
+
+
+@pytest.mark.parametrize("lang,compiler", [("c", "gcc"), ("c++", "g++")])
+def test_header_compiles_as_c_and_cpp(tmp_path, lang, compiler):
+    """include/mi355attn.h is a plain C header (usable from C and C++)."""
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("compiler or HIP headers not available")
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "mi355attn.h"\nint main(void) { return attn_abi_version() == 2 ? 0 : 1; }\n')
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    r = subprocess.run([compiler, "-fsyntax-only", "-x", lang, "-D__HIP_PLATFORM_AMD__", "-I", inc,
+                        "-I", "/opt/rocm/include", str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
