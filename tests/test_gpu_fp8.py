@@ -23,7 +23,8 @@ def ta():
     return m
 
 
-@pytest.mark.parametrize("B,hkv,S,d", [(2, 2, 100, 128), (1, 3, 64, 64), (3, 1, 5, 16)])
+@pytest.mark.parametrize("B,hkv,S,d", [(2, 2, 100, 128), (1, 3, 64, 64), (3, 1, 5, 16),
+                                       (2, 1, 70, 576)])
 def test_quantiser_bitwise(ta, oracle_mod, B, hkv, S, d):
     g = torch.Generator().manual_seed(400 + S)
     x = torch.randn(B, hkv, S, d, generator=g) * torch.exp(2 * torch.randn(B, hkv, S, 1, generator=g))
