@@ -15,14 +15,19 @@ backward (dQ, dK, dV) of the Llama-3-8B prefill in TFLOP/s, counting
 10*d_h FLOP per visible pair (five products), and the 70B decode on a paged
 cache (pages of 64 positions in a random order) in GB/s.
 
+The tiny fp32 parity configuration (B=1, T=64, 4/2 heads, d_h=16) is timed
+too, in microseconds: it is one kernel launch.
+
 Inputs are seeded synthetic N(0,1) tensors (workloads.py), resident in HBM
 before timing.  W untimed warm-up steps, then exactly K timed steps between
-two device synchronisations; kernel durations come from HIP events recorded
-on the stream the kernels run on.  One JSON line is printed.
+two device synchronisations; HIP events recorded on the stream the kernels
+run on bracket every call, giving the mean (``ms``, ``ms_per_step``) and the
+median (``median_ms``) per call.  The JSON line also names the library file
+that was timed and its hash.  One JSON line is printed.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|backward|decode|decode-paged|decode-fp8|rope|mla|swa-mha|
-                            swa-mqa|copy]
+                    [--only prefill|swa-mha|swa-mqa|backward|decode|decode-fp8|rope|
+                            decode-paged|mla|tiny-fp32|copy]
 
 ``--only copy`` times a plain 1 GiB device copy instead: it is the
 calibration run for rocprofv3's HBM byte counters, not an attention bench.
@@ -58,20 +63,30 @@ def prefill_flops(shape) -> int:
                                                                         shape.window)
 
 
-def _events_time(torch, fn, steps, warmup, stream):
+LAST_MEDIAN_MS = {}
+
+
+def _events_time(torch, fn, steps, warmup, stream, key=None):
+    """Mean milliseconds per call over `steps` back-to-back calls (HIP events
+    on `stream` around each call), after `warmup` untimed calls; the median
+    of the per-call durations is kept in LAST_MEDIAN_MS[key]."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall
+    per_call = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    n = len(per_call)
+    median = (per_call[n // 2] if n % 2 else 0.5 * (per_call[n // 2 - 1] + per_call[n // 2]))
+    if key is not None:
+        LAST_MEDIAN_MS[key] = median
+    return ev[0].elapsed_time(ev[steps]) / steps, wall
 
 
 def bench_prefill(torch, ta, W, shape, steps, warmup):
@@ -80,7 +95,7 @@ def bench_prefill(torch, ta, W, shape, steps, warmup):
     stream = torch.cuda.current_stream()
     fn = lambda: ta.attn_prefill(q, k, v, causal=shape.causal, window=shape.window,
                                  scale=shape.scale, o=o)
-    ms, wall = _events_time(torch, fn, steps, warmup, stream)
+    ms, wall = _events_time(torch, fn, steps, warmup, stream, key=shape.name)
     flops = prefill_flops(shape)
     tflops = flops / (ms * 1e-3) / 1e12
     del q, k, v, o
@@ -108,7 +123,7 @@ def bench_backward(torch, ta, W, shape, steps, warmup):
     fn = lambda: ta.attn_prefill_backward(q, k, v, o, do, lse, causal=shape.causal,
                                           window=shape.window, scale=shape.scale, dq=dq, dk=dk,
                                           dv=dv, workspace=ws)
-    ms, wall = _events_time(torch, fn, steps, warmup, stream)
+    ms, wall = _events_time(torch, fn, steps, warmup, stream, key="backward")
     flops = backward_flops(shape)
     tflops = flops / (ms * 1e-3) / 1e12
     del q, k, v, do, o, lse, dq, dk, dv, ws
@@ -125,7 +140,7 @@ def bench_decode(torch, ta, W, steps, warmup):
                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     fn = lambda: ta.attn_decode(q, kc, vc, lens_d, scale=s.scale, o=o, workspace=ws)
-    ms, wall = _events_time(torch, fn, steps, warmup, stream)
+    ms, wall = _events_time(torch, fn, steps, warmup, stream, key="decode")
     total_len = int(lens.sum())
     cache_bytes = total_len * 2 * s.h_kv * s.d_h * 2
     io_bytes = 2 * s.B * s.h_q * s.d_h * 2
@@ -152,7 +167,7 @@ def bench_decode_paged(torch, ta, W, steps, warmup, page_size=64):
                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     fn = lambda: ta.attn_decode_paged(q, kp, vp, lens_d, table, scale=s.scale, o=o, workspace=ws)
-    ms, wall = _events_time(torch, fn, steps, warmup, stream)
+    ms, wall = _events_time(torch, fn, steps, warmup, stream, key="decode_paged")
     total_len = int(lens.sum())
     nbytes = total_len * 2 * s.h_kv * s.d_h * 2 + 2 * s.B * s.h_q * s.d_h * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -176,7 +191,7 @@ def bench_decode_fp8(torch, ta, W, steps, warmup):
                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     fn = lambda: ta.attn_decode_fp8(q, k8, v8, ks, vs, lens_d, scale=s.scale, o=o, workspace=ws)
-    ms, wall = _events_time(torch, fn, steps, warmup, stream)
+    ms, wall = _events_time(torch, fn, steps, warmup, stream, key="decode_fp8")
     total_len = int(lens.sum())
     tiles = int(((lens + 31) // 32).sum())
     nbytes = (total_len * 2 * s.h_kv * s.d_h + tiles * 2 * s.h_kv * 4 +
@@ -194,7 +209,7 @@ def bench_rope(torch, ta, W, steps, warmup):
     q, k, v = W.prefill_inputs(s, seed=0, device="cuda", gen_device="cuda")
     del v
     stream = torch.cuda.current_stream()
-    ms, wall = _events_time(torch, lambda: ta.attn_rope_qk(q, k, base=5e5), steps, warmup, stream)
+    ms, wall = _events_time(torch, lambda: ta.attn_rope_qk(q, k, base=5e5), steps, warmup, stream, key="rope")
     nbytes = 2 * (q.numel() + k.numel()) * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     del q, k
@@ -208,7 +223,7 @@ def bench_copy(torch, steps, warmup, nbytes=1 << 30):
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     stream = torch.cuda.current_stream()
-    ms, wall = _events_time(torch, lambda: dst.copy_(src), steps, warmup, stream)
+    ms, wall = _events_time(torch, lambda: dst.copy_(src), steps, warmup, stream, key="copy")
     gbs = 2 * nbytes / (ms * 1e-3) / 1e9
     del src, dst
     return {"ms": ms, "wall_s": wall, "bytes": 2 * nbytes, "gbs": gbs,
@@ -230,7 +245,7 @@ def bench_mla(torch, ta, W, steps, warmup, copies=3):
         it[0] += 1
         ta.mla_decode(q, c, lens, scale=s.scale, o=o, workspace=ws)
 
-    ms, wall = _events_time(torch, fn, steps, warmup, stream)
+    ms, wall = _events_time(torch, fn, steps, warmup, stream, key="mla")
     total = int(sum(int(l.sum()) for _, _, l in sets[:1]))
     cache_bytes = total * (s.d_c + s.d_r) * 2
     io_bytes = s.B * s.H * (s.d_c + s.d_r) * 2 + s.B * s.H * s.d_c * 2
@@ -242,9 +257,36 @@ def bench_mla(torch, ta, W, steps, warmup, copies=3):
             "tflops": flops / (ms * 1e-3) / 1e12, "cache_copies_rotated": copies}
 
 
+def bench_tiny_fp32(torch, ta, W, steps, warmup):
+    """The tiny fp32 causal GQA prefill (B=1, T=64, 4/2 heads, d_h=16): a
+    parity case whose time is one kernel launch; reported in microseconds."""
+    s = W.TINY_FP32
+    q, k, v = W.prefill_inputs(s, seed=0, device="cuda")
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    fn = lambda: ta.attn_prefill(q, k, v, causal=True, scale=s.scale, o=o)
+    ms, wall = _events_time(torch, fn, max(steps, 20), warmup, stream, key="tiny_fp32")
+    return {"ms": ms, "wall_s": wall, "flops": prefill_flops(s)}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline_prefill(W, shape, budget_s=20.0):
     """The fp64 oracle on a bounded sample of the prefill workload: all heads
-    of a growing set of query rows until the budget is used."""
+    of a growing set of query rows until the budget is used.  `value` counts
+    the visible (query, key) pairs, 4 d_h FLOP each, like the GPU figure; the
+    oracle as written scores every key of a row before masking, so it also
+    does 2 d_h FLOP per masked pair (`flops_as_written`)."""
     import numpy as np
     import oracle
     oracle.build(force=False)
@@ -266,11 +308,30 @@ def cpu_baseline_prefill(W, shape, budget_s=20.0):
         lo = max(0, r - shape.window + 1) if shape.window else 0
         hi = r + 1 if shape.causal else shape.T
         vis += hi - lo
-    flops = 4 * shape.B * shape.h_q * shape.d_h * vis
+    per_pair = shape.B * shape.h_q * shape.d_h
+    flops = 4 * per_pair * vis
+    as_written = 2 * per_pair * (len(rows) * shape.T + vis)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "host_cpus_available": len(os.sched_getaffinity(0)),
+            "wall_s": round(elapsed, 2), "flops_visible_pairs": flops,
+            "flops_as_written": as_written,
+            "value_as_written": as_written / elapsed / 1e12,
             "sample": f"{len(rows)} evenly spaced query rows x all {shape.h_q} heads of "
                       f"the workload ({elapsed:.1f} s, fp64, full score rows materialised)"}
+
+
+def _library_info(ta):
+    import hashlib
+    path = os.path.abspath(ta.LIB_PATH)
+    with open(path, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    return {"path": os.path.relpath(path, os.path.dirname(os.path.abspath(__file__))),
+            "sha256_16": digest[:16]}
+
+
+BENCHES = ("prefill", "swa-mha", "swa-mqa", "backward", "decode", "decode-fp8", "rope",
+           "decode-paged", "mla", "tiny-fp32", "copy")
 
 
 def main(argv=None):
@@ -279,10 +340,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default=None,
-                    choices=["prefill", "backward", "decode", "decode-paged", "decode-fp8", "rope", "mla",
-                             "swa-mha",
-                             "swa-mqa", "copy"])
+    ap.add_argument("--only", default=None, choices=BENCHES)
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -301,120 +359,119 @@ def main(argv=None):
 
     only = args.only
     shape = W.LLAMA3_8B_PREFILL
+    steps, warmup = args.steps, args.warmup
+    runs = {
+        "prefill": lambda: bench_prefill(torch, ta, W, shape, steps, warmup),
+        "swa-mha": lambda: bench_prefill(torch, ta, W, W.SWA_MHA, steps, warmup),
+        "swa-mqa": lambda: bench_prefill(torch, ta, W, W.SWA_MQA, steps, warmup),
+        "backward": lambda: bench_backward(torch, ta, W, shape, steps, warmup),
+        "decode": lambda: bench_decode(torch, ta, W, steps, warmup),
+        "decode-fp8": lambda: bench_decode_fp8(torch, ta, W, steps, warmup),
+        "rope": lambda: bench_rope(torch, ta, W, steps, warmup),
+        "decode-paged": lambda: bench_decode_paged(torch, ta, W, steps, warmup),
+        "mla": lambda: bench_mla(torch, ta, W, steps, warmup),
+        "tiny-fp32": lambda: bench_tiny_fp32(torch, ta, W, steps, warmup),
+        "copy": lambda: bench_copy(torch, steps, warmup),
+    }
+    median_key = {"prefill": shape.name, "swa-mha": W.SWA_MHA.name, "swa-mqa": W.SWA_MQA.name}
+    selected = [only] if only else [b for b in BENCHES if b != "copy"]
     out = {}
-    if only in (None, "prefill"):
-        out["prefill"] = bench_prefill(torch, ta, W, shape, args.steps, args.warmup)
-        print(f"[bench] prefill {out['prefill']['ms']:.3f} ms "
-              f"{out['prefill']['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    if only in (None, "swa-mha"):
-        out["swa_mha"] = bench_prefill(torch, ta, W, W.SWA_MHA, args.steps, args.warmup)
-    if only in (None, "swa-mqa"):
-        out["swa_mqa"] = bench_prefill(torch, ta, W, W.SWA_MQA, args.steps, args.warmup)
-    if only in (None, "backward"):
-        out["backward"] = bench_backward(torch, ta, W, shape, args.steps, args.warmup)
-        print(f"[bench] backward {out['backward']['ms']:.3f} ms "
-              f"{out['backward']['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    if only == "copy":
-        out["copy"] = bench_copy(torch, args.steps, args.warmup)
-    if only in (None, "decode"):
-        out["decode"] = bench_decode(torch, ta, W, args.steps, args.warmup)
-        print(f"[bench] decode {out['decode']['ms']:.3f} ms {out['decode']['gbs']:.0f} GB/s",
-              file=sys.stderr, flush=True)
-    if only in (None, "decode-fp8"):
-        out["decode_fp8"] = bench_decode_fp8(torch, ta, W, args.steps, args.warmup)
-        print(f"[bench] decode (fp8 cache) {out['decode_fp8']['ms']:.3f} ms "
-              f"{out['decode_fp8']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
-    if only in (None, "rope"):
-        out["rope"] = bench_rope(torch, ta, W, args.steps, args.warmup)
-        print(f"[bench] rope (q and k) {out['rope']['ms']:.3f} ms {out['rope']['gbs']:.0f} GB/s",
-              file=sys.stderr, flush=True)
-    if only in (None, "decode-paged"):
-        out["decode_paged"] = bench_decode_paged(torch, ta, W, args.steps, args.warmup)
-        print(f"[bench] decode (paged) {out['decode_paged']['ms']:.3f} ms "
-              f"{out['decode_paged']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
-    if only in (None, "mla"):
-        out["mla"] = bench_mla(torch, ta, W, args.steps, args.warmup)
-        print(f"[bench] mla {out['mla']['ms']:.3f} ms {out['mla']['gbs']:.0f} GB/s",
+    for name in selected:
+        r = runs[name]()
+        r["median_ms"] = LAST_MEDIAN_MS[median_key.get(name, name.replace("-", "_"))]
+        out[name] = r
+        rate = (f"{r['tflops']:.1f} TFLOP/s" if "tflops" in r and "gbs" not in r else
+                f"{r['gbs']:.0f} GB/s" if "gbs" in r else "")
+        print(f"[bench] {name} {r['ms']:.4f} ms (median {r['median_ms']:.4f}) {rate}",
               file=sys.stderr, flush=True)
 
     line = {
         "metric": "GQA prefill TFLOP/s + decode KV-cache GB/s, as % of MI355X peak, d_h=128",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic N(0,1), seeded",
+        "timing": "HIP events on the library's stream around each call; ms = mean of the timed "
+                  "calls, median_ms = their median",
+        "library": _library_info(ta),
     }
-    if "prefill" in out:
-        p = out["prefill"]
+    first = selected[0]
+    r = out[first]
+    if first == "prefill":
         line.update({
-            "value": round(p["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(p["ms"], 4),
+            "value": round(r["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms"], 4),
+            "median_ms": round(r["median_ms"], 4),
             "config": {"workload": "Llama-3-8B-shaped causal GQA prefill", "B": shape.B,
                        "seq_len": shape.T, "h_q": shape.h_q, "h_kv": shape.h_kv,
-                       "d_h": shape.d_h, "causal": True, "flops_counted": p["flops"]},
-            "roofline": {"bound": "mfma", "achieved": round(p["tflops"], 2),
+                       "d_h": shape.d_h, "causal": True, "flops_counted": r["flops"]},
+            "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(p["frac_bf16_peak"], 4),
+                         "frac": round(r["frac_bf16_peak"], 4),
                          "traffic": PREFILL_TRAFFIC_BYTES},
         })
+    elif "gbs" in r:
+        line.update({"value": round(r["gbs"], 1), "unit": "GB/s", "ms_per_step": round(r["ms"], 4),
+                     "median_ms": round(r["median_ms"], 4), "config": {"workload": first},
+                     "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(r["frac_hbm_peak"], 4), "traffic": None}})
+    elif "frac_bf16_peak" in r:
+        line.update({"value": round(r["tflops"], 2), "unit": "TFLOP/s",
+                     "ms_per_step": round(r["ms"], 4), "median_ms": round(r["median_ms"], 4),
+                     "config": {"workload": first},
+                     "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2),
+                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(r["frac_bf16_peak"], 4), "traffic": None}})
     else:
-        key = next(iter(out))
-        r = out[key]
-        if "gbs" in r:
-            line.update({"value": round(r["gbs"], 1), "unit": "GB/s", "ms_per_step": round(r["ms"], 4),
-                         "config": {"workload": key},
-                         "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1),
-                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": round(r["frac_hbm_peak"], 4), "traffic": None}})
-        else:
-            line.update({"value": round(r["tflops"], 2), "unit": "TFLOP/s",
-                         "ms_per_step": round(r["ms"], 4), "config": {"workload": key},
-                         "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2),
-                                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                      "frac": round(r["frac_bf16_peak"], 4), "traffic": None}})
-    if "decode" in out:
-        d = out["decode"]
-        line["decode"] = {"workload": "70B-shaped GQA decode, B=64, 64/8 heads, S_max=32768",
-                          "ms": round(d["ms"], 4), "GB_s": round(d["gbs"], 1),
-                          "frac_hbm_peak": round(d["frac_hbm_peak"], 4), "bytes": d["bytes"],
-                          "sum_len": d["sum_len"]}
-    for key, shp, name in (("swa_mha", W.SWA_MHA, "sliding-window MHA prefill, B=4, T=4096, 32/32 heads, W=1024"),
-                           ("swa_mqa", W.SWA_MQA, "sliding-window MQA prefill, B=4, T=4096, 32/1 heads, W=1024")):
-        if key in out and key != next(iter(out)):
-            r = out[key]
-            line[key] = {"workload": name, "ms": round(r["ms"], 4), "TFLOP_s": round(r["tflops"], 2),
-                         "frac_bf16_peak": round(r["frac_bf16_peak"], 4), "flops": r["flops"]}
-    if "decode_paged" in out and next(iter(out)) != "decode_paged":
-        d = out["decode_paged"]
-        line["decode_paged"] = {"workload": "70B-shaped GQA decode, cache in pages of "
-                                            f"{d['page_size']} positions (random page order)",
-                                "ms": round(d["ms"], 4), "GB_s": round(d["gbs"], 1),
-                                "frac_hbm_peak": round(d["frac_hbm_peak"], 4), "bytes": d["bytes"]}
-    if "decode_fp8" in out and next(iter(out)) != "decode_fp8":
-        d = out["decode_fp8"]
-        line["decode_fp8"] = {"workload": "70B-shaped GQA decode, cache in FP8 E4M3 (one scale per "
-                                          "32 positions of a head)",
-                              "ms": round(d["ms"], 4), "GB_s": round(d["gbs"], 1),
-                              "frac_hbm_peak": round(d["frac_hbm_peak"], 4), "bytes": d["bytes"]}
-        if "decode" in out:
-            line["decode_fp8"]["speedup_vs_bf16_cache"] = round(out["decode"]["ms"] / d["ms"], 3)
-    if "rope" in out and next(iter(out)) != "rope":
-        d = out["rope"]
-        line["rope"] = {"workload": "RoPE of the Llama-3-8B prefill's q and k in place (32/8 heads, "
-                                    "T=8192, base 5e5)",
-                        "ms": round(d["ms"], 4), "GB_s": round(d["gbs"], 1),
-                        "frac_hbm_peak": round(d["frac_hbm_peak"], 4), "bytes": d["bytes"]}
-    if "backward" in out and next(iter(out)) != "backward":
-        r = out["backward"]
-        line["backward"] = {"workload": "Llama-3-8B-shaped causal GQA prefill backward (dQ, dK, dV)",
-                            "ms": round(r["ms"], 4), "TFLOP_s": round(r["tflops"], 2),
-                            "frac_bf16_peak": round(r["frac_bf16_peak"], 4), "flops": r["flops"]}
-    if "mla" in out:
-        m = out["mla"]
-        line["mla"] = {"workload": "DeepSeek-V3-shaped MLA absorbed decode, B=32, 128 heads, S=16384",
-                       "ms": round(m["ms"], 4), "GB_s": round(m["gbs"], 1),
-                       "frac_hbm_peak": round(m["frac_hbm_peak"], 4), "bytes": m["bytes"],
-                       "TFLOP_s": round(m["tflops"], 2),
-                       "cache_copies_rotated": m["cache_copies_rotated"]}
-    if not args.no_cpu_baseline and "prefill" in out:
+        line.update({"value": round(r["ms"] * 1e3, 2), "unit": "us", "higher_is_better": False,
+                     "ms_per_step": round(r["ms"], 4), "median_ms": round(r["median_ms"], 4),
+                     "config": {"workload": first}})
+
+    def sub(key, workload, **extra):
+        d = out[key]
+        o = {"workload": workload, "ms": round(d["ms"], 4), "median_ms": round(d["median_ms"], 4)}
+        if "gbs" in d:
+            o.update({"GB_s": round(d["gbs"], 1), "frac_hbm_peak": round(d["frac_hbm_peak"], 4),
+                      "bytes": d["bytes"]})
+        elif "frac_bf16_peak" in d:
+            o.update({"TFLOP_s": round(d["tflops"], 2),
+                      "frac_bf16_peak": round(d["frac_bf16_peak"], 4), "flops": d["flops"]})
+        o.update(extra)
+        line[key.replace("-", "_")] = o
+
+    names = {
+        "swa-mha": "sliding-window MHA prefill, B=4, T=4096, 32/32 heads, W=1024",
+        "swa-mqa": "sliding-window MQA prefill, B=4, T=4096, 32/1 heads, W=1024",
+        "backward": "Llama-3-8B-shaped causal GQA prefill backward (dQ, dK, dV)",
+        "decode": "70B-shaped GQA decode, B=64, 64/8 heads, S_max=32768",
+        "decode-fp8": "70B-shaped GQA decode, cache in FP8 E4M3 (one scale per 32 positions of "
+                      "a head)",
+        "rope": "RoPE of the Llama-3-8B prefill's q and k in place (32/8 heads, T=8192, base 5e5)",
+        "decode-paged": "70B-shaped GQA decode, cache in pages of 64 positions (random page "
+                        "order)",
+        "mla": "DeepSeek-V3-shaped MLA absorbed decode, B=32, 128 heads, S=16384",
+    }
+    for key in out:
+        if key == first or key == "copy":
+            continue
+        if key == "tiny-fp32":
+            d = out[key]
+            line["tiny_fp32"] = {"workload": "tiny causal GQA prefill, fp32, B=1, T=64, 4/2 heads, "
+                                             "d_h=16 (one launch; parity case); per call, "
+                                             "including the binding's host-side launch overhead",
+                                 "us": round(d["ms"] * 1e3, 2),
+                                 "median_us": round(d["median_ms"] * 1e3, 2),
+                                 "flops": d["flops"]}
+            continue
+        extra = {}
+        if key == "decode":
+            extra["sum_len"] = out[key]["sum_len"]
+        if key == "decode-fp8" and "decode" in out:
+            extra["speedup_vs_bf16_cache"] = round(out["decode"]["ms"] / out[key]["ms"], 3)
+        if key == "mla":
+            extra.update({"TFLOP_s": round(out[key]["tflops"], 2),
+                          "cache_copies_rotated": out[key]["cache_copies_rotated"]})
+        sub(key, names[key], **extra)
+    if not args.no_cpu_baseline and first == "prefill":
         line["cpu_baseline"] = cpu_baseline_prefill(W, shape)
     print(json.dumps(line), flush=True)
     return 0

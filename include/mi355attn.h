@@ -266,7 +266,11 @@ attn_status_t mla_decode_paged(const void *q, const void *kv_pages, void *o, flo
  *   scales : [B, h_kv, ceil(S / 32)] float32 (written)
  * scale = amax / 448 over the tile (1 for an all-zero tile, fp32 division);
  * code = E4M3 nearest to x / scale (fp32 division, ties to even, magnitudes
- * clamped to 448).  The last tile may hold fewer than 32 positions.  A paged
+ * clamped to 448).  Non-finite input: E4M3 has no infinities, so a NaN or
+ * +-inf is stored as the NaN code 0x7f (0xff when its sign bit is set) and
+ * reads back as NaN; amax runs over the tile's finite values only, so such
+ * an entry changes no other code or scale (a tile with no finite nonzero
+ * value gets scale 1).  The last tile may hold fewer than 32 positions.  A paged
  * cache [num_pages, h_kv, page_size, d_h] is quantised by passing B =
  * num_pages, S = page_size.  d_h must be a multiple of 8.
  *

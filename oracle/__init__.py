@@ -266,7 +266,8 @@ def fp8_e4m3_value(code: int) -> float:
 
 
 def fp8_e4m3_encode(v: float) -> int:
-    """Nearest E4M3 code to the float32 value v (ties to even, saturating)."""
+    """Nearest E4M3 code to the float32 value v (ties to even, saturating);
+    NaN and +-infinity give the NaN code 0x7f / 0xff with v's sign."""
     return int(_load().oracle_fp8_e4m3_encode(float(np.float32(v))))
 
 
@@ -280,8 +281,9 @@ def fp8_dequantize(codes, scales, *, tile: int = 32) -> np.ndarray:
 
 def quantize_kv_fp8(x):
     """Per-tile FP8 quantisation of a cache x:[B, h_kv, S, d]: 32 positions of
-    one head per tile, scale = amax / 448.  Returns (codes uint8 like x,
-    scales float32 [B, h_kv, ceil(S/32)])."""
+    one head per tile, scale = amax / 448 with amax over the tile's finite
+    values; NaN and +-infinity are stored as the NaN code with their sign.
+    Returns (codes uint8 like x, scales float32 [B, h_kv, ceil(S/32)])."""
     x = _f32(x)
     B, hkv, S, d = x.shape
     codes = np.zeros(x.shape, dtype=np.uint8)

@@ -468,6 +468,13 @@ int oracle_max_threads(void)
  * tensor (K and V separately).  scale = amax / 448 (fp32 division; 1 for an
  * all-zero tile), code = nearest E4M3 value of x / scale (fp32 division),
  * ties to the even code, magnitudes above 448 saturated to 448.
+ *
+ * Non-finite input (reading): E4M3 has no infinities; its only non-finite
+ * value is NaN (codes 0x7f and 0xff).  A NaN or an infinity is stored as
+ * that NaN code with the input's sign bit, so it stays non-finite when the
+ * cache is read back.  The scale is a statistic of the values the type can
+ * hold, so amax runs over the tile's finite values only: a non-finite entry
+ * leaves the codes of its finite neighbours unchanged.
  */
 static double fp8_value(unsigned code)
 {
@@ -480,9 +487,11 @@ static double fp8_value(unsigned code)
 
 double oracle_fp8_e4m3_value(int code) { return fp8_value((unsigned)code & 0xffu); }
 
-/* nearest finite E4M3 code to v, ties to the even code, saturating */
+/* nearest finite E4M3 code to v, ties to the even code, saturating;
+ * NaN and +-infinity give the NaN code with v's sign */
 static unsigned char fp8_encode(float v)
 {
+    if (isnan(v) || isinf(v)) return (unsigned char)(signbit(v) ? 0xffu : 0x7fu);
     const double a = fabs((double)v);
     unsigned best = 0;
     double best_err = INFINITY;
@@ -516,14 +525,14 @@ int oracle_quantize_kv_fp8(const float *x, unsigned char *codes, float *scales,
         for (long r = r0; r < r1; ++r)
             for (int e = 0; e < d; ++e) {
                 const float a = fabsf(xb[r * d + e]);
-                if (a > amax) amax = a;
+                if (isfinite(a) && a > amax) amax = a;
             }
         const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
         scales[u] = sc;
         for (long r = r0; r < r1; ++r)
             for (int e = 0; e < d; ++e) {
-                const float y = xb[r * d + e] / sc;
-                cb[r * d + e] = fp8_encode(y);
+                const float xv = xb[r * d + e];
+                cb[r * d + e] = fp8_encode(isfinite(xv) ? xv / sc : xv);
             }
     }
     return 0;

@@ -31,6 +31,11 @@ def test_quantiser_bitwise(ta, oracle_mod, B, hkv, S, d):
     x[0, 0, :min(S, 32)] = 0.0                      # an all-zero tile
     if S > 40:
         x[-1, -1, 40, 3] = 1e4                      # one tile dominated by an outlier
+    if S > 64:                                      # non-finite entries: the signed NaN code,
+        x[0, -1, 33, 1] = float("nan")              # scale over the finite values only
+        x[-1, 0, 64, 0] = -float("inf")
+        x[-1, 0, 65, d - 1] = float("inf")
+        x[0, 0, 2, 2] = -float("nan")               # inside the all-zero tile
     x = x.to(torch.bfloat16)
     print(f"[case] quantise {B},{hkv},{S},{d}", flush=True)
     codes, scales = ta.attn_quantize_kv_fp8(x.cuda())

@@ -9,6 +9,9 @@ production-engine notes).  Pinned against things other than the oracle:
   * encoding against torch's float32 -> float8_e4m3fn conversion, on a dense
     grid (normals, subnormals, exact ties) and on random values;
   * hand-worked ties to even;
+  * non-finite input: NaN and +-infinity against torch's cast (the NaN code
+    with the input's sign), and a tile holding them quantises its finite
+    entries exactly as the same tile with zeros in their place;
   * the quantiser against the same recipe written with torch ops (amax / 448,
     division, cast), bit for bit, including a ragged last tile and an
     all-zero tile;
@@ -129,3 +132,41 @@ def test_paged_fp8_gathers_codes_and_scales(oracle_mod):
     o1, l1 = oracle_mod.decode_paged_fp8(q, kp, vp, ksp, vsp, table, lens, scale=0.35)
     o2, l2 = oracle_mod.decode_fp8(q, k8, v8, ks, vs, lens, scale=0.35)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_non_finite_values_encode_as_the_signed_nan_code(oracle_mod):
+    """E4M3 has no infinities; torch's float32 -> float8_e4m3fn cast stores
+    NaN and +-inf as the NaN code with the input's sign bit."""
+    vals = np.array([np.nan, -np.nan, np.inf, -np.inf], dtype=np.float32)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle_mod.fp8_e4m3_encode(x) for x in vals], dtype=np.uint8)
+    assert list(ref) == [0x7f, 0xff, 0x7f, 0xff]
+    assert np.array_equal(got, ref)
+
+
+def test_non_finite_entries_leave_their_tile_neighbours_unchanged(oracle_mod):
+    """The tile scale is taken over finite values only: putting NaN / +-inf
+    into a tile changes the codes of exactly those entries (to the signed
+    NaN code) and neither the scale nor any other code."""
+    rng = np.random.default_rng(21)
+    B, hkv, S, d = 2, 2, 70, 16
+    x = (rng.standard_normal((B, hkv, S, d)) * 3).astype(np.float32)
+    bad = np.zeros(x.shape, dtype=bool)
+    spots = [(0, 0, 3, 5, np.nan), (0, 1, 40, 0, np.inf), (1, 0, 69, 15, -np.inf),
+             (1, 1, 31, 7, -np.nan), (1, 1, 0, 0, np.inf)]
+    xb = x.copy()
+    xz = x.copy()
+    for b, h, s_, e, val in spots:
+        xb[b, h, s_, e] = val
+        xz[b, h, s_, e] = 0.0
+        bad[b, h, s_, e] = True
+    cb, sb = oracle_mod.quantize_kv_fp8(xb)
+    cz, sz = oracle_mod.quantize_kv_fp8(xz)
+    assert np.array_equal(sb, sz)
+    assert np.array_equal(cb[~bad], cz[~bad])
+    want = [0xff if np.signbit(val) else 0x7f for *_, val in spots]
+    assert [int(cb[b, h, s_, e]) for b, h, s_, e, _ in spots] == want
+    # a tile of nothing but non-finite values gets scale 1
+    xa = np.full((1, 1, 32, 8), np.inf, dtype=np.float32)
+    ca, sa = oracle_mod.quantize_kv_fp8(xa)
+    assert sa[0, 0, 0] == 1.0 and np.all(ca == 0x7f)

@@ -155,6 +155,18 @@ def _sinks(sinks, h_q, device):
     return sinks
 
 
+def _lse_out(lse, B, hq, device, return_lse):
+    """The optional [B, h_q] fp32 log-sum-exp output of a decode call: checked
+    here because the merge kernel writes all B * h_q entries."""
+    if lse is None and return_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, device)
+        if lse.numel() != B * hq:
+            raise ValueError(f"lse must hold B * h_q = {B * hq} values, got {lse.numel()}")
+    return lse
+
+
 def attn_prefill(q, k, v, *, causal: bool = True, window: int = 0, scale=None,
                  sinks=None, o=None, lse=None, return_lse: bool = False):
     """q:[B,h_q,T,d]  k,v:[B,h_kv,T,d] (bf16 or fp32, contiguous, same device).
@@ -277,10 +289,7 @@ def attn_decode(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale=None,
     _require(o, "o", torch.bfloat16, q.device)
     if o.numel() != q.numel():
         raise ValueError("o shape mismatch")
-    if lse is None and return_lse:
-        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _require(lse, "lse", torch.float32, q.device)
+    lse = _lse_out(lse, B, hq, q.device, return_lse)
     need = lib.attn_decode_workspace_size(B, S_max, hq, hkv, d, int(split_tokens))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -318,10 +327,7 @@ def mla_decode(q, kv_cache, seq_lens, *, d_c: int = 512, d_r: int = 64, scale: f
     _require(o, "o", torch.bfloat16, q.device)
     if o.numel() != B * H * d_c:
         raise ValueError("o shape mismatch")
-    if lse is None and return_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _require(lse, "lse", torch.float32, q.device)
+    lse = _lse_out(lse, B, H, q.device, return_lse)
     need = lib.mla_decode_workspace_size(B, S_max, H, d_c, d_r, int(split_tokens))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -362,10 +368,7 @@ def attn_decode_paged(q, k_pages, v_pages, seq_lens, block_table, *, window: int
     _require(o, "o", torch.bfloat16, q.device)
     if o.numel() != q.numel():
         raise ValueError("o shape mismatch")
-    if lse is None and return_lse:
-        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _require(lse, "lse", torch.float32, q.device)
+    lse = _lse_out(lse, B, hq, q.device, return_lse)
     need = lib.attn_decode_paged_workspace_size(B, max_blocks, page_size, hq, hkv, d,
                                                 int(split_tokens))
     if workspace is None:
@@ -400,10 +403,7 @@ def mla_decode_paged(q, kv_pages, seq_lens, block_table, *, d_c: int = 512, d_r:
     _require(o, "o", torch.bfloat16, q.device)
     if o.numel() != B * H * d_c:
         raise ValueError("o shape mismatch")
-    if lse is None and return_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _require(lse, "lse", torch.float32, q.device)
+    lse = _lse_out(lse, B, H, q.device, return_lse)
     need = lib.mla_decode_paged_workspace_size(B, max_blocks, page_size, H, d_c, d_r,
                                                int(split_tokens))
     if workspace is None:
@@ -444,13 +444,7 @@ def _decode_out(q, B, hq, o, lse, return_lse):
     _require(o, "o", torch.bfloat16, q.device)
     if o.numel() != q.numel():
         raise ValueError("o shape mismatch")
-    if lse is None and return_lse:
-        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _require(lse, "lse", torch.float32, q.device)
-        if lse.numel() != B * hq:
-            raise ValueError("lse shape mismatch")
-    return o, lse
+    return o, _lse_out(lse, B, hq, q.device, return_lse)
 
 
 def attn_decode_fp8(q, k_codes, v_codes, k_scales, v_scales, seq_lens, *, window: int = 0,

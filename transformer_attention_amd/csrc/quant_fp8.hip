@@ -9,6 +9,9 @@
 // kernel streams, so each streamed tile carries one scale.  An all-zero tile
 // gets scale 1.  The division is IEEE fp32 and the cast rounds to nearest
 // even (v_cvt_pk_fp8_f32), with magnitudes clamped to 448 first.
+// E4M3 has no infinities: a NaN or +-inf input is stored as the NaN code
+// (0x7f, or 0xff with the sign bit set), and the tile's amax runs over its
+// finite values only, so such an entry changes no other code of its tile.
 //
 // One wave per tile.  For d_h <= 128 a tile (at most 4096 values) is held in
 // registers (eight 16-byte loads per lane), so the cache is read once: the
@@ -23,14 +26,32 @@ namespace {
 
 constexpr int TILE = 32;
 
+// |x| of a finite value, 0 for NaN and +-inf (the amax statistic)
+__device__ __forceinline__ float finite_abs(float x) {
+    const float a = fabsf(x);
+    return a < __builtin_inff() ? a : 0.f;
+}
+
 __device__ __forceinline__ i32x2 encode8(const bf16x8 v, float sc) {
     float y[8];
+    unsigned nan_bytes[2] = {0u, 0u}, nan_mask[2] = {0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf((float)v[e] / sc, -448.0f), 448.0f);
+    for (int e = 0; e < 8; ++e) {
+        const float x = (float)v[e];
+        const bool fin = fabsf(x) < __builtin_inff();
+        y[e] = fin ? fminf(fmaxf(x / sc, -448.0f), 448.0f) : 0.f;
+        if (!fin) {
+            const unsigned sh = 8u * (e & 3);
+            nan_mask[e >> 2] |= 0xffu << sh;
+            nan_bytes[e >> 2] |= (__builtin_bit_cast(unsigned, x) >> 31 ? 0xffu : 0x7fu) << sh;
+        }
+    }
     int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
     int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+    w0 = (int)(((unsigned)w0 & ~nan_mask[0]) | nan_bytes[0]);
+    w1 = (int)(((unsigned)w1 & ~nan_mask[1]) | nan_bytes[1]);
     return i32x2{w0, w1};
 }
 
@@ -55,7 +76,7 @@ __global__ __launch_bounds__(256) void quantize_kv_fp8_kernel(const __bf16 *x, u
             const int c = 8 * lane + 512 * i;
             buf[i] = c < n ? __builtin_bit_cast(bf16x8, ldg16(x + base + c)) : bf16x8{};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)buf[i][e]));
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, finite_abs((float)buf[i][e]));
         }
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
@@ -70,7 +91,7 @@ __global__ __launch_bounds__(256) void quantize_kv_fp8_kernel(const __bf16 *x, u
         for (int c = 8 * lane; c < n; c += 512) {
             const bf16x8 v = __builtin_bit_cast(bf16x8, ldg16(x + base + c));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, finite_abs((float)v[e]));
         }
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
