@@ -5,8 +5,29 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "mi355attn.h"
 #include "kernels.h"
+
+namespace mi355 {
+
+hipError_t ensure_dynamic_lds(const void *kernel, int bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::mutex mu;
+    static std::set<std::pair<int, const void *>> done;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({dev, kernel})) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.insert({dev, kernel});
+    return e;
+}
+
+}  // namespace mi355
 
 namespace {
 
@@ -149,15 +170,11 @@ size_t attn_decode_workspace_size(int B, int S_max, int h_q, int h_kv, int d_h, 
     return split_ws_bytes((long long)B * h_q, ns, d_h) + align_up((size_t)(B + 1) * sizeof(int32_t), 256);
 }
 
-// Shared by the four GQA decode entry points (contiguous / paged, bf16 /
-// FP8): everything after the layout-specific checks.
-static attn_status_t decode_launch(const void *q, const void *k, const void *v, const float *k_scales,
-                                   const float *v_scales, void *o, float *lse,
-                                   const int32_t *seq_lens, const int32_t *block_table, int B,
-                                   int S_max, int max_blocks, int page_size, int num_pages, int h_q,
-                                   int h_kv, int d_h, int window, float scale, const float *sinks,
-                                   int split_tokens, void *workspace, size_t workspace_bytes,
-                                   hipStream_t stream) {
+// The argument checks every GQA decode entry point shares (host only: no
+// HIP call is made before they pass).
+static attn_status_t decode_check(const void *q, const void *k, const void *v, const void *o,
+                                  const int32_t *seq_lens, int B, int S_max, int h_q, int h_kv,
+                                  int d_h, int window, float scale, int split_tokens) {
     if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(o) || bad_ptr(seq_lens))
         return ATTN_ERR_INVALID_ARG;
     if (B <= 0 || S_max <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
@@ -165,6 +182,21 @@ static attn_status_t decode_launch(const void *q, const void *k, const void *v, 
     if (split_tokens < 0 || split_tokens % 64) return ATTN_ERR_INVALID_ARG;
     if (d_h != 128) return ATTN_ERR_UNSUPPORTED;
     if (B > 65535 || h_kv * ((h_q / h_kv + 15) / 16) > 65535) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+// Shared by the GQA decode entry points (contiguous / paged, bf16 / FP8):
+// everything after the layout-specific checks.
+static attn_status_t decode_launch(const void *q, const void *k, const void *v, const float *k_scales,
+                                   const float *v_scales, void *o, float *lse,
+                                   const int32_t *seq_lens, const int32_t *block_table, int B,
+                                   int S_max, int max_blocks, int page_size, int num_pages, int h_q,
+                                   int h_kv, int d_h, int window, float scale, const float *sinks,
+                                   int split_tokens, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    const attn_status_t checked = decode_check(q, k, v, o, seq_lens, B, S_max, h_q, h_kv, d_h,
+                                               window, scale, split_tokens);
+    if (checked != ATTN_OK) return checked;
     const int split = resolve_decode_split(split_tokens, B, S_max, h_q, h_kv, k_scales != nullptr);
     const int ns = (S_max + split - 1) / split;
     const size_t need = attn_decode_workspace_size(B, S_max, h_q, h_kv, d_h, split_tokens);

@@ -596,18 +596,14 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
                        a.split, a.hkv * p.n_hchunk, a.plan);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    static bool attr_set = false;
-    if (!attr_set) {
+    {
         const void *fns[4] = {(const void *)decode_bf16_d128_kernel<false, false>,
                               (const void *)decode_bf16_d128_kernel<true, false>,
                               (const void *)decode_bf16_d128_kernel<false, true>,
                               (const void *)decode_bf16_d128_kernel<true, true>};
-        const int lds[4] = {Layout<false>::lds, Layout<false>::lds, Layout<true>::lds, Layout<true>::lds};
-        for (int i = 0; i < 4; ++i) {
-            e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds[i]);
-            if (e != hipSuccess) return e;
-        }
-        attr_set = true;
+        const int which = (a.k_scales ? 2 : 0) + (a.block_table ? 1 : 0);
+        e = ensure_dynamic_lds(fns[which], a.k_scales ? Layout<true>::lds : Layout<false>::lds);
+        if (e != hipSuccess) return e;
     }
     // persistent grid: one workgroup per CU (its LDS takes most of the CU),
     // never more workgroups than the largest possible number of units needs

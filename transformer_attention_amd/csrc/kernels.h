@@ -7,6 +7,12 @@
 
 namespace mi355 {
 
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per (device, kernel) in the process; safe to call from several threads.
+// The limit belongs to the function on each device, so a process that
+// launches on several GPUs sets it on every one of them.
+hipError_t ensure_dynamic_lds(const void *kernel, int bytes);
+
 struct PrefillArgs {
     const void *q, *k, *v;
     void *o;
@@ -84,9 +90,6 @@ struct MlaArgs {
 };
 hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream);
 
-// Merge of split partials: o[b,h,:] (bf16) and lse[b,h] (natural log, may be
-// null) from ws_o/ws_lse over the ceil(len_b / split) splits of sequence b;
-// sinks (per head, may be null) adds a sink logit to each merged denominator.
 // Rotary position embedding of q [B, hq, T, row_q] and k [B, hk, T, row_k]
 // (k may be null with hk = 0), dimensions [rope_offset, rope_offset +
 // rope_dim) of each row, in place.
@@ -103,6 +106,9 @@ hipError_t launch_rope_qk(const RopeArgs &a, hipStream_t stream);
 // scale per 32 positions of a head (amax / 448), codes [B*hkv, S, d].
 hipError_t launch_quantize_kv_fp8(const void *x, void *codes, float *scales, long long n_heads,
                                   int S, int d, hipStream_t stream);
+// Merge of split partials: o[b,h,:] (bf16) and lse[b,h] (natural log, may be
+// null) from ws_o/ws_lse over the ceil(len_b / split) splits of sequence b;
+// sinks (per head, may be null) adds a sink logit to each merged denominator.
 hipError_t launch_split_combine(const float *ws_o, const float *ws_lse,
                                 const int32_t *seq_lens, void *o, float *lse,
                                 int B, int H, int dv, int S_max, int split,

@@ -343,16 +343,9 @@ hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream) {
     p.split = a.split;
     p.n_split_max = a.n_split_max;
     p.scale_log2 = a.scale * kLog2e;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)mla_decode_kernel<false>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute((const void *)mla_decode_kernel<true>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    hipError_t e = a.block_table ? ensure_dynamic_lds((const void *)mla_decode_kernel<true>, LDS_BYTES)
+                                 : ensure_dynamic_lds((const void *)mla_decode_kernel<false>, LDS_BYTES);
+    if (e != hipSuccess) return e;
     p.n_hchunk = (a.H + HPC - 1) / HPC;
     const long long n_wg = (long long)a.B * a.n_split_max * p.n_hchunk;
     if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -362,7 +355,7 @@ hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream) {
     else
         hipLaunchKernelGGL(mla_decode_kernel<false>, dim3((unsigned)n_wg), dim3(64 * NW), LDS_BYTES,
                            stream, p);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_combine(a.ws_o, a.ws_lse, a.seq_lens, a.o, a.lse, a.B, a.H, DC, a.S_max,
                                 a.split, a.n_split_max, a.sinks, stream);

@@ -590,13 +590,8 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs &a, hipStream_t stream) {
     p.window = a.window;
     p.scale_log2 = a.scale * kLog2e;
     p.sinks = a.sinks;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)prefill_bf16_d128_kernel<NB, KB, NST>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    hipError_t e = ensure_dynamic_lds((const void *)prefill_bf16_d128_kernel<NB, KB, NST>, LDS_BYTES);
+    if (e != hipSuccess) return e;
     const long long nblocks = (long long)p.n_row_blocks * p.n_head_groups;
     if (nblocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((prefill_bf16_d128_kernel<NB, KB, NST>), dim3((unsigned)nblocks), dim3(64 * NW),

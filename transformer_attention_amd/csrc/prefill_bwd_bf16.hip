@@ -618,19 +618,13 @@ hipError_t launch_prefill_bwd_bf16_d128(const PrefillBwdArgs &a, hipStream_t str
     p.n_row_blocks = (a.T + p.rows_per_wg - 1) / p.rows_per_wg;
     p.n_head_groups = a.B * a.hkv * (p.G / p.hpw);
 
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, KA_LDS);
-        if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute((const void *)bwd_dq_kernel,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, KB_LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    hipError_t e = ensure_dynamic_lds((const void *)bwd_dkdv_kernel, KA_LDS);
+    if (e != hipSuccess) return e;
+    e = ensure_dynamic_lds((const void *)bwd_dq_kernel, KB_LDS);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)(a.Tpad / 16), (unsigned)(a.B * a.hq)), dim3(256),
                        0, stream, p);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long n_kb = ((long long)a.T + KA_KEYS - 1) / KA_KEYS;
     const long long n_a = n_kb * a.B * a.hkv;
