@@ -331,6 +331,32 @@ attn_status_t attn_rope_qk(void *q, void *k, const int32_t *positions, int B, in
                            int h_q, int h_k, int row_q, int row_k, int rope_offset,
                            int rope_dim, float base, attn_dtype_t dtype, hipStream_t stream);
 
+/*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, semantics and results as attn_decode
+ * without the workspace: the split partials and the work plan live in a
+ * static device array of MI355ATTN_DECODE_NOALLOC_SCRATCH_BYTES bytes that
+ * the library holds on every GPU it runs on until the process ends.  The
+ * call allocates nothing.
+ *
+ * Limit: the problem's workspace, attn_decode_workspace_size(B, S_max, h_q,
+ * h_kv, d_h, split_tokens), must fit in the array; otherwise the call
+ * returns ATTN_ERR_WORKSPACE and launches nothing.  The 70B-shaped decode
+ * (B = 64, h_q / h_kv = 64 / 8, d_h = 128, S_max = 32768) needs about 34 MB
+ * at the default split; a larger split_tokens shrinks the need.  All calls
+ * on one GPU share the array: calls that overlap in time on
+ * one GPU (different streams, or different threads without ordering) race
+ * and must be ordered by the caller.  Nothing in the array needs to start at
+ * zero; each call writes what it reads.
+ */
+#define MI355ATTN_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+attn_status_t attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  void *o, float *lse, const int32_t *seq_lens,
+                                  int B, int S_max, int h_q, int h_kv, int d_h,
+                                  int window, float scale, const float *sinks, int split_tokens,
+                                  hipStream_t stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *attn_status_string(attn_status_t status);
 

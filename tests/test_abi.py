@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
               "attn_decode", "mla_decode", "attn_decode_workspace_size",
               "attn_decode_paged", "attn_decode_paged_workspace_size", "mla_decode_paged",
               "mla_decode_paged_workspace_size", "attn_quantize_kv_fp8", "attn_decode_fp8",
-              "attn_decode_paged_fp8", "attn_rope_qk",
+              "attn_decode_paged_fp8", "attn_rope_qk", "attn_decode_noalloc",
               "mla_decode_workspace_size", "attn_status_string", "attn_abi_version"):
         assert n in names, n
 
@@ -126,6 +126,30 @@ def test_decode_validation(lib):
     assert need > 0
     assert dec(wsb=need - 1) == 3
     assert lib.attn_decode_workspace_size(2, 64, 7, 2, 128, 0) == 0
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode: the same argument checks as attn_decode,
+    and a problem whose workspace exceeds the static array is refused with
+    ATTN_ERR_WORKSPACE before anything is launched."""
+    def dec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lens=FAKE, B=2, S=64, hq=8, hkv=2, d=128,
+                 window=0, scale=0.1, split=0)
+        a.update(kw)
+        return lib.attn_decode_noalloc(a["q"], a["k"], a["v"], a["o"], None, a["lens"], a["B"],
+                                       a["S"], a["hq"], a["hkv"], a["d"], a["window"], a["scale"],
+                                       None, a["split"], None)
+    assert dec(lens=None) == 1
+    assert dec(q=None) == 1
+    assert dec(hq=7) == 1
+    assert dec(window=-3) == 1
+    assert dec(split=100) == 1
+    assert dec(scale=float("nan")) == 1
+    assert dec(d=64) == 2
+    limit = 64 << 20
+    assert lib.attn_decode_workspace_size(64, 8192, 64, 8, 128, 64) > limit
+    assert dec(B=64, S=8192, hq=64, hkv=8, split=64) == 3
+    assert dec(B=64, S=8192, hq=64, hkv=8, split=64, d=64) == 2
 
 
 def test_fp8_validation(lib):

@@ -45,6 +45,7 @@ EXPORTED_SYMBOLS = (
     "mla_decode", "mla_decode_workspace_size", "attn_decode_paged",
     "attn_decode_paged_workspace_size", "mla_decode_paged", "mla_decode_paged_workspace_size",
     "attn_quantize_kv_fp8", "attn_decode_fp8", "attn_decode_paged_fp8", "attn_rope_qk",
+    "attn_decode_noalloc",
     "attn_status_string",
     "attn_abi_version",
 )
@@ -100,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P,
                                           I, P, Z, P]
     lib.attn_decode_paged_fp8.restype = I
+    lib.attn_decode_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, P, I, P]
+    lib.attn_decode_noalloc.restype = I
     lib.attn_rope_qk.argtypes = [P, P, P, I, I, I, I, I, I, I, I, F, I, P]
     lib.attn_rope_qk.restype = I
     lib.attn_status_string.argtypes = [I]
@@ -301,6 +304,39 @@ def attn_decode(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale=None,
                          float(scale), _ptr(sinks), int(split_tokens), _ptr(workspace), ws_bytes,
                          _stream(q.device))
     _check(st, "attn_decode")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+# Size of the static device array attn_decode_noalloc works in (bytes).
+DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, seq_lens, *, window: int = 0, scale=None,
+                        sinks=None, split_tokens: int = 0, o=None, lse=None,
+                        return_lse: bool = False):
+    """attn_decode without a workspace: the library's static device array holds
+    the partials, so the C call allocates nothing (pass ``o`` and ``lse`` to
+    keep this wrapper from allocating them).  Raises AttnError
+    (ATTN_ERR_WORKSPACE) when the problem's workspace exceeds
+    DECODE_NOALLOC_SCRATCH_BYTES.  Calls overlapping on one GPU race."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16)
+    _require(k_cache, "k_cache", torch.bfloat16, q.device, 4)
+    _require(v_cache, "v_cache", torch.bfloat16, q.device, 4)
+    _require(seq_lens, "seq_lens", torch.int32, q.device, 1)
+    B, hkv, S_max, d = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("v_cache shape mismatch")
+    hq = q.shape[1]
+    if q.numel() != B * hq * d or q.shape[0] != B or q.shape[-1] != d or seq_lens.shape[0] != B:
+        raise ValueError("q / seq_lens shape mismatch")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o, lse = _decode_out(q, B, hq, o, lse, return_lse)
+    st = lib.attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
+                                 _ptr(seq_lens), B, S_max, hq, hkv, d, int(window), float(scale),
+                                 _ptr(_sinks(sinks, hq, q.device)), int(split_tokens),
+                                 _stream(q.device))
+    _check(st, "attn_decode_noalloc")
     return (o, lse) if (return_lse or lse is not None) else o
 
 

@@ -185,8 +185,9 @@ static attn_status_t decode_check(const void *q, const void *k, const void *v, c
     return ATTN_OK;
 }
 
-// Shared by the GQA decode entry points (contiguous / paged, bf16 / FP8):
-// everything after the layout-specific checks.
+// Shared by the GQA decode entry points (contiguous / paged, bf16 / FP8,
+// caller workspace or static scratch): everything after the layout-specific
+// checks.
 static attn_status_t decode_launch(const void *q, const void *k, const void *v, const float *k_scales,
                                    const float *v_scales, void *o, float *lse,
                                    const int32_t *seq_lens, const int32_t *block_table, int B,
@@ -378,3 +379,61 @@ attn_status_t mla_decode_paged(const void *q, const void *kv_pages, void *o, flo
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// attn_decode_noalloc: attn_decode with its workspace in a static device
+// array instead of caller memory, for callers that cannot allocate.
+//
+// `scratch` is a file-scope device array; every GPU the library runs on
+// holds its own copy from module load until the process ends.  In host code
+// its name is only a host-side stand-in, so the device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and only
+// that address is ever handed to kernels.  The decode writes the whole plan
+// and every partial it later reads within the same call (stream-ordered), so
+// nothing in the array has to start at zero and the contents left by a
+// previous call are never read.  Calls that overlap on one GPU share the
+// array and race; the caller orders them.
+namespace {
+
+__device__ __align__(256) unsigned char scratch[MI355ATTN_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_addr[kMaxDevices] = {};
+
+attn_status_t device_scratch(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return ATTN_ERR_HIP;
+        scratch_addr[dev] = p;
+    }
+    *out = scratch_addr[dev];
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" attn_status_t attn_decode_noalloc(const void *q, const void *k_cache,
+                                             const void *v_cache, void *o, float *lse,
+                                             const int32_t *seq_lens, int B, int S_max, int h_q,
+                                             int h_kv, int d_h, int window, float scale,
+                                             const float *sinks, int split_tokens,
+                                             hipStream_t stream) {
+    const attn_status_t checked = decode_check(q, k_cache, v_cache, o, seq_lens, B, S_max, h_q,
+                                               h_kv, d_h, window, scale, split_tokens);
+    if (checked != ATTN_OK) return checked;
+    const size_t need = attn_decode_workspace_size(B, S_max, h_q, h_kv, d_h, split_tokens);
+    if (need == 0 || need > (size_t)MI355ATTN_DECODE_NOALLOC_SCRATCH_BYTES)
+        return ATTN_ERR_WORKSPACE;                  // does not fit: nothing is launched
+    void *ws = nullptr;
+    const attn_status_t st = device_scratch(&ws);
+    if (st != ATTN_OK) return st;
+    return decode_launch(q, k_cache, v_cache, nullptr, nullptr, o, lse, seq_lens, nullptr, B, S_max,
+                         0, 0, 0, h_q, h_kv, d_h, window, scale, sinks, split_tokens, ws,
+                         (size_t)MI355ATTN_DECODE_NOALLOC_SCRATCH_BYTES, stream);
+}
