@@ -79,6 +79,8 @@ def _load():
     lib.oracle_quantize_kv_fp8.restype = I
     lib.oracle_decode_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, P]
     lib.oracle_decode_fp8.restype = I
+    lib.oracle_mla_decode_fp8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, D, P, I, I]
+    lib.oracle_mla_decode_fp8.restype = I
     lib.oracle_rope.argtypes = [P, P, P, I, I, I, I, I, I, D]
     lib.oracle_rope.restype = I
     lib.oracle_merge_partials.argtypes = [P, P, I, I, P, P]
@@ -316,6 +318,36 @@ def decode_fp8(q, k8, v8, k_scales, v_scales, seq_lens, *, window: int = 0, scal
                                    B, S_max, hq, hkv, d, int(window), float(scale), sk_ptr)
     if rc != 0:
         raise ValueError("oracle_decode_fp8: invalid shape")
+    return o, lse
+
+
+def mla_decode_fp8(q, codes, scales, seq_lens, *, d_c: int, d_r: int, scale: float,
+                   split: int, tile: int = 64, sinks=None):
+    """MLA absorbed decode with FP8 attention (the pages' FA3 FP8 recipe):
+    the query quantised per head (amax / 448), the cache given as E4M3 codes
+    [B, S_max, d_c+d_r] with one scale per 32 tokens [B, ceil(S_max/32)],
+    both products on the dequantised codes, the probabilities quantised to
+    E4M3 against each chunk's running reference (chunks of ``split`` tokens,
+    compute tiles of ``tile`` tokens) with the value scale folded in, the
+    denominator from the unquantised probabilities.  Returns (o:[B,H,d_c],
+    lse:[B,H])."""
+    q = _f32(q)
+    B, H, dk = q.shape
+    codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    assert dk == d_c + d_r and codes.shape[0] == B and codes.shape[2] == dk
+    S_max = codes.shape[1]
+    sc = _f32(scales).reshape(B, -1)
+    assert sc.shape[1] == (S_max + 31) // 32
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    assert lens.shape == (B,)
+    o = np.zeros((B, H, d_c), dtype=np.float64)
+    lse = np.zeros((B, H), dtype=np.float64)
+    sk, sk_ptr = _sinks(sinks, H)
+    rc = _load().oracle_mla_decode_fp8(_ptr(q), _ptr(codes), _ptr(sc), _ptr(lens), _ptr(o),
+                                       _ptr(lse), B, S_max, H, d_c, d_r, float(scale), sk_ptr,
+                                       int(split), int(tile))
+    if rc != 0:
+        raise ValueError("oracle_mla_decode_fp8: invalid shape")
     return o, lse
 
 

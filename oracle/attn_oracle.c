@@ -508,6 +508,21 @@ static unsigned char fp8_encode(float v)
 
 int oracle_fp8_e4m3_encode(float v) { return (int)fp8_encode(v); }
 
+/* One tile of n values: scale = amax / 448 over its finite values (1 when
+ * that is 0), codes = E4M3 of x / scale. */
+static float quantize_block(const float *x, long n, unsigned char *codes)
+{
+    float amax = 0.0f;
+    for (long i = 0; i < n; ++i) {
+        const float a = fabsf(x[i]);
+        if (isfinite(a) && a > amax) amax = a;
+    }
+    const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+    for (long i = 0; i < n; ++i)
+        codes[i] = fp8_encode(isfinite(x[i]) ? x[i] / sc : x[i]);
+    return sc;
+}
+
 /* x:[B,hkv,S,d] float -> codes:[B,hkv,S,d], scales:[B,hkv,ceil(S/32)] */
 int oracle_quantize_kv_fp8(const float *x, unsigned char *codes, float *scales,
                            int B, int hkv, int S, int d)
@@ -519,21 +534,8 @@ int oracle_quantize_kv_fp8(const float *x, unsigned char *codes, float *scales,
     for (long u = 0; u < tiles; ++u) {
         const long t = u % nt, bg = u / nt;
         const long r0 = t * 32, r1 = (r0 + 32 < S) ? r0 + 32 : S;
-        const float *xb = x + (bg * (long)S) * d;
-        unsigned char *cb = codes + (bg * (long)S) * d;
-        float amax = 0.0f;
-        for (long r = r0; r < r1; ++r)
-            for (int e = 0; e < d; ++e) {
-                const float a = fabsf(xb[r * d + e]);
-                if (isfinite(a) && a > amax) amax = a;
-            }
-        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-        scales[u] = sc;
-        for (long r = r0; r < r1; ++r)
-            for (int e = 0; e < d; ++e) {
-                const float xv = xb[r * d + e];
-                cb[r * d + e] = fp8_encode(isfinite(xv) ? xv / sc : xv);
-            }
+        const long off = (bg * (long)S + r0) * d;
+        scales[u] = quantize_block(x + off, (r1 - r0) * d, codes + off);
     }
     return 0;
 }
@@ -585,6 +587,118 @@ int oracle_decode_fp8(const float *q, const unsigned char *k8, const unsigned ch
             if (lse) lse[u] = l_out;
         }
         free(s); free(p); free(vis); free(vdq);
+    }
+    return 0;
+}
+
+/*
+ * MLA absorbed decode in FP8: the pages' FP8 attention ("Flash Attention 3
+ * and Multi-Headed Latent Attention", the FP8 attention section and the
+ * FA3FP8BlockProcessor listing: q, k, v and p quantised to E4M3 per tile
+ * with scale = amax / 448, both products on FP8 operands, the results
+ * dequantised by the scales) applied to the MLA decode of "Attention
+ * Engineering ...", section 3, as that page's combined FA3 + MLA kernel box
+ * suggests.  Steps, per sequence b and head h:
+ *
+ *  1. the query row (576 values) is one tile: sq = amax / 448, q8 = E4M3(q /
+ *     sq) -- the quantiser above on a one-row tile;
+ *  2. the cache holds codes c8 with one scale sc per 32 tokens (the FP8 cache
+ *     quantiser above with h_kv = 1); the value of token j is the first d_c
+ *     entries of its dequantised row, so k and v share their codes and scale;
+ *  3. s_j = scale * sq * sc_j * sum_d q8[d] c8_j[d] (exact dequantised
+ *     product), in natural units;
+ *  4. the weight of token j in the value product carries its tile's value
+ *     scale: y_j = s_j log2(e) + log2(sc_j).  The keys of the sequence are
+ *     taken in chunks of `split` tokens and each chunk in compute tiles of
+ *     `tile` tokens in order; the chunk's reference R is the running max of
+ *     y over the tiles seen so far (moved before a tile's weights are
+ *     taken);
+ *  5. p is quantised to E4M3 against that reference: P8_j = E4M3(min(448,
+ *     448 * 2^(y_j - R))), so the largest weight seen is stored as 448 (the
+ *     pages' p / (amax / 448)) with the value scale folded in; when R moves,
+ *     the chunk's accumulated numerator is rescaled by 2^(R_old - R_new);
+ *  6. the numerator N = sum_j P8_j * c8_j[0:d_c] (exact), the denominator the
+ *     unquantised l = sum_j 2^(s_j log2(e) - R) (the page normalises the
+ *     softmax before quantising p); the chunk's output N / (448 l) and
+ *     log-sum-exp (R + log2 l) ln 2;
+ *  7. chunks merge by their log-sum-exp (oracle_merge_partials), with the
+ *     sink logit as one more part of zero output.
+ * q:[B,H,dc+dr] float (bf16 values); c8:[B,S_max,dc+dr] codes; cs:[B,
+ * ceil(S_max/32)] scales; o:[B,H,dc]; lse:[B,H].  split and tile are
+ * positive multiples of 32, tile divides split.
+ */
+int oracle_mla_decode_fp8(const float *q, const unsigned char *c8, const float *cs,
+                          const int *seq_lens, double *o, double *lse,
+                          int B, int S_max, int H, int dc, int dr, double scale,
+                          const float *sinks, int split, int tile)
+{
+    if (B < 0 || S_max < 0 || H <= 0 || dc <= 0 || dr < 0 || split <= 0 || tile <= 0 ||
+        split % 32 || tile % 32 || split % tile) return -1;
+    const int dk = dc + dr;
+    const long nt = (S_max + 31) / 32;
+    const long units = (long)B * H;
+    const double log2e = 1.0 / log(2.0);
+#pragma omp parallel
+    {
+        unsigned char *q8 = (unsigned char *)malloc(dk);
+        double *num = (double *)malloc(sizeof(double) * dc);
+        double *y = (double *)malloc(sizeof(double) * (tile > 0 ? tile : 1));
+        double *sn = (double *)malloc(sizeof(double) * (tile > 0 ? tile : 1));
+        const long max_parts = S_max / split + 2;
+        double *part_o = (double *)malloc(sizeof(double) * max_parts * dc);
+        double *part_l = (double *)malloc(sizeof(double) * max_parts);
+#pragma omp for schedule(dynamic, 1)
+        for (long u = 0; u < units; ++u) {
+            const long b = u / H, h = u % H;
+            long len = seq_lens[b];
+            if (len < 0) len = 0;
+            if (len > S_max) len = S_max;
+            const double sq = (double)quantize_block(q + u * dk, dk, q8);
+            int np = 0;
+            for (long c0 = 0; c0 < len; c0 += split) {
+                const long c1 = c0 + split < len ? c0 + split : len;
+                double R = -INFINITY, l = 0.0;
+                for (int d = 0; d < dc; ++d) num[d] = 0.0;
+                for (long t0 = c0; t0 < c1; t0 += tile) {
+                    const long t1 = t0 + tile < c1 ? t0 + tile : c1;
+                    double tmax = -INFINITY;
+                    for (long j = t0; j < t1; ++j) {
+                        const unsigned char *row = c8 + ((size_t)b * S_max + j) * dk;
+                        const double sc = (double)cs[b * nt + j / 32];
+                        double acc = 0.0;
+                        for (int d = 0; d < dk; ++d) acc += fp8_value(q8[d]) * fp8_value(row[d]);
+                        sn[j - t0] = scale * sq * sc * acc;
+                        y[j - t0] = sn[j - t0] * log2e + log2(sc);
+                        if (y[j - t0] > tmax) tmax = y[j - t0];
+                    }
+                    if (tmax > R) {                 /* move the reference, rescale */
+                        const double f = R == -INFINITY ? 0.0 : exp2(R - tmax);
+                        for (int d = 0; d < dc; ++d) num[d] *= f;
+                        l *= f;
+                        R = tmax;
+                    }
+                    for (long j = t0; j < t1; ++j) {
+                        const unsigned char *row = c8 + ((size_t)b * S_max + j) * dk;
+                        double w = 448.0 * exp2(y[j - t0] - R);
+                        if (w > 448.0) w = 448.0;
+                        const double pq = fp8_value(fp8_encode((float)w));
+                        for (int d = 0; d < dc; ++d) num[d] += pq * fp8_value(row[d]);
+                        l += exp2(sn[j - t0] * log2e - R);
+                    }
+                }
+                for (int d = 0; d < dc; ++d) part_o[(long)np * dc + d] = num[d] / (448.0 * l);
+                part_l[np] = (R + log2(l)) * log(2.0);
+                ++np;
+            }
+            if (sinks && sinks[h] != -INFINITY) {
+                for (int d = 0; d < dc; ++d) part_o[(long)np * dc + d] = 0.0;
+                part_l[np++] = (double)sinks[h];
+            }
+            double l_out;
+            oracle_merge_partials(part_o, part_l, np, dc, o + u * dc, &l_out);
+            if (lse) lse[u] = l_out;
+        }
+        free(q8); free(num); free(y); free(sn); free(part_o); free(part_l);
     }
     return 0;
 }
