@@ -257,6 +257,43 @@ def bench_mla(torch, ta, W, steps, warmup, copies=3):
             "tflops": flops / (ms * 1e-3) / 1e12, "cache_copies_rotated": copies}
 
 
+def bench_mla_fp8(torch, ta, W, steps, warmup, copies=3):
+    """The DeepSeek-V3-shaped MLA decode with FP8 attention: each of the
+    rotated bf16 caches quantised to E4M3 (one scale per 32 tokens) by the
+    library's quantiser before timing; the query is quantised inside the
+    call.  Bytes: codes + scales + q + o."""
+    s = W.DSV3_MLA_DECODE
+    dk = s.d_c + s.d_r
+    sets = []
+    for i in range(copies):
+        q, c, lens = W.mla_inputs(s, seed=i, device="cuda", gen_device="cuda")
+        codes, scales = ta.attn_quantize_kv_fp8(c.view(s.B, 1, s.S_max, dk))
+        del c
+        sets.append((q, codes.view(s.B, s.S_max, dk), scales.view(s.B, -1), lens.cuda()))
+    o = torch.empty((s.B, s.H, s.d_c), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(ta.mla_decode_fp8_workspace_size(s.B, s.S_max, s.H, s.d_c, s.d_r),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    it = [0]
+
+    def fn():
+        q, codes, scales, lens = sets[it[0] % copies]
+        it[0] += 1
+        ta.mla_decode_fp8(q, codes, scales, lens, scale=s.scale, o=o, workspace=ws)
+
+    ms, wall = _events_time(torch, fn, steps, warmup, stream, key="mla_fp8")
+    lens0 = sets[0][3]
+    total = int(lens0.sum())
+    n_scales = int(((lens0 + 31) // 32).sum())
+    nbytes = total * dk + n_scales * 4 + s.B * s.H * dk * 2 + s.B * s.H * s.d_c * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    flops = 2 * s.H * total * (s.d_c + s.d_r + s.d_c)
+    del sets, o, ws
+    return {"ms": ms, "wall_s": wall, "bytes": nbytes, "gbs": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS, "tflops": flops / (ms * 1e-3) / 1e12,
+            "cache_copies_rotated": copies}
+
+
 def bench_tiny_fp32(torch, ta, W, steps, warmup):
     """The tiny fp32 causal GQA prefill (B=1, T=64, 4/2 heads, d_h=16): a
     parity case whose time is one kernel launch; reported in microseconds."""
@@ -331,7 +368,7 @@ def _library_info(ta):
 
 
 BENCHES = ("prefill", "swa-mha", "swa-mqa", "backward", "decode", "decode-fp8", "rope",
-           "decode-paged", "mla", "tiny-fp32", "copy")
+           "decode-paged", "mla", "mla-fp8", "tiny-fp32", "copy")
 
 
 def main(argv=None):
@@ -370,6 +407,7 @@ def main(argv=None):
         "rope": lambda: bench_rope(torch, ta, W, steps, warmup),
         "decode-paged": lambda: bench_decode_paged(torch, ta, W, steps, warmup),
         "mla": lambda: bench_mla(torch, ta, W, steps, warmup),
+        "mla-fp8": lambda: bench_mla_fp8(torch, ta, W, steps, warmup),
         "tiny-fp32": lambda: bench_tiny_fp32(torch, ta, W, steps, warmup),
         "copy": lambda: bench_copy(torch, steps, warmup),
     }
@@ -449,6 +487,9 @@ def main(argv=None):
         "decode-paged": "70B-shaped GQA decode, cache in pages of 64 positions (random page "
                         "order)",
         "mla": "DeepSeek-V3-shaped MLA absorbed decode, B=32, 128 heads, S=16384",
+        "mla-fp8": "DeepSeek-V3-shaped MLA absorbed decode with FP8 attention (E4M3 cache with "
+                   "one scale per 32 tokens, q and p quantised in the call, FP8 MFMA); lower "
+                   "precision, not the bf16 workload",
     }
     for key in out:
         if key == first or key == "copy":
@@ -467,9 +508,13 @@ def main(argv=None):
             extra["sum_len"] = out[key]["sum_len"]
         if key == "decode-fp8" and "decode" in out:
             extra["speedup_vs_bf16_cache"] = round(out["decode"]["ms"] / out[key]["ms"], 3)
-        if key == "mla":
+        if key in ("mla", "mla-fp8"):
             extra.update({"TFLOP_s": round(out[key]["tflops"], 2),
                           "cache_copies_rotated": out[key]["cache_copies_rotated"]})
+        if key == "mla-fp8":
+            extra["dtype"] = "fp8 e4m3 operands, fp32 accumulate"
+            if "mla" in out:
+                extra["speedup_vs_bf16"] = round(out["mla"]["ms"] / out[key]["ms"], 3)
         sub(key, names[key], **extra)
     if not args.no_cpu_baseline and first == "prefill":
         line["cpu_baseline"] = cpu_baseline_prefill(W, shape)

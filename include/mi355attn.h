@@ -308,6 +308,42 @@ attn_status_t attn_decode_paged_fp8(const void *q, const void *k_pages, const vo
                                     hipStream_t stream);
 
 /*
+ * mla_decode_fp8 -- mla_decode with FP8 attention: the pages' FP8 recipe
+ * ("Flash Attention 3 and Multi-Headed Latent Attention", the FP8 attention
+ * section and its per-tile block processor: q, k, v and p quantised to E4M3
+ * with scale amax / 448, both products on FP8 operands, dequantised by the
+ * scales) on the absorbed MLA decode.  Both products run on E4M3 matrix
+ * instructions with fp32 accumulation.
+ *
+ *   q         : [B, h_q, d_c + d_r] bf16 (read); quantised inside the call,
+ *               one scale per head row (amax / 448, as attn_quantize_kv_fp8
+ *               does for a one-row tile)
+ *   kv_codes  : [B, S_max, d_c + d_r] uint8 E4M3 codes (read; only tokens
+ *               < seq_lens[b])
+ *   kv_scales : [B, ceil(S_max / 32)] float32: one scale per 32 tokens, the
+ *               layout attn_quantize_kv_fp8 writes for a [B, 1, S_max, d_c +
+ *               d_r] cache (h_kv = 1)
+ *   o, lse, seq_lens, scale, sinks, split_tokens : as mla_decode
+ * s_j = scale * sq * sc_j * (q8 . c8_j).  The probabilities are quantised to
+ * E4M3 in 64-token tiles against each chunk's reference R, with the value
+ * scale of their token folded in: e_j = 448 * 2^(y_j - R), y_j = s_j log2(e)
+ * + log2(sc_j); when a tile's max of y exceeds R, R moves to that max plus 3
+ * (log2 units), so no weight passes 448.  The output is sum_j e_j c8_j /
+ * (448 l) with the unquantised denominator l = sum_j 2^(s_j log2(e) - R).
+ * Chunks (and the sink) merge by their log-sum-exp.  The result differs from
+ * mla_decode on the same values by the E4M3 rounding of q, the cache and p.
+ * workspace: at least mla_decode_fp8_workspace_size(...) bytes (the split
+ * partials plus the query codes and scales).  Supported: d_c = 512, d_r = 64.
+ */
+size_t mla_decode_fp8_workspace_size(int B, int S_max, int h_q, int d_c, int d_r,
+                                     int split_tokens);
+attn_status_t mla_decode_fp8(const void *q, const void *kv_codes, const float *kv_scales,
+                             void *o, float *lse, const int32_t *seq_lens, int B, int S_max,
+                             int h_q, int d_c, int d_r, float scale, const float *sinks,
+                             int split_tokens, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
  * attn_rope_qk -- rotary position embedding of the queries and keys, in
  * place, in one launch ("Attention Engineering ...", section 1: pair j of
  * the rotated dimensions, (x_{2j}, x_{2j+1}), is rotated as a complex number

@@ -327,8 +327,9 @@ def mla_decode_fp8(q, codes, scales, seq_lens, *, d_c: int, d_r: int, scale: flo
     the query quantised per head (amax / 448), the cache given as E4M3 codes
     [B, S_max, d_c+d_r] with one scale per 32 tokens [B, ceil(S_max/32)],
     both products on the dequantised codes, the probabilities quantised to
-    E4M3 against each chunk's running reference (chunks of ``split`` tokens,
-    compute tiles of ``tile`` tokens) with the value scale folded in, the
+    E4M3 against each chunk's reference (chunks of ``split`` tokens, compute
+    tiles of ``tile`` tokens; the reference moves to a tile's max plus 3, in
+    log2 units, when the tile exceeds it) with the value scale folded in, the
     denominator from the unquantised probabilities.  Returns (o:[B,H,d_c],
     lse:[B,H])."""
     q = _f32(q)

@@ -610,13 +610,16 @@ int oracle_decode_fp8(const float *q, const unsigned char *k8, const unsigned ch
  *  4. the weight of token j in the value product carries its tile's value
  *     scale: y_j = s_j log2(e) + log2(sc_j).  The keys of the sequence are
  *     taken in chunks of `split` tokens and each chunk in compute tiles of
- *     `tile` tokens in order; the chunk's reference R is the running max of
- *     y over the tiles seen so far (moved before a tile's weights are
- *     taken);
+ *     `tile` tokens in order.  The chunk keeps a reference R (-inf at the
+ *     start); before a tile's weights are taken, if the tile's max of y
+ *     exceeds R, R moves to that max plus MLA_FP8_HEADROOM (3, in log2
+ *     units), so later tiles may rise by up to 2^3 before R has to move
+ *     again;
  *  5. p is quantised to E4M3 against that reference: P8_j = E4M3(min(448,
- *     448 * 2^(y_j - R))), so the largest weight seen is stored as 448 (the
- *     pages' p / (amax / 448)) with the value scale folded in; when R moves,
- *     the chunk's accumulated numerator is rescaled by 2^(R_old - R_new);
+ *     448 * 2^(y_j - R))) with the value scale folded in -- the pages' p /
+ *     (amax / 448) with amax bounded by 2^R (every y_j <= R, so no weight
+ *     passes 448); when R moves, the chunk's accumulated numerator and
+ *     denominator are rescaled by 2^(R_old - R_new);
  *  6. the numerator N = sum_j P8_j * c8_j[0:d_c] (exact), the denominator the
  *     unquantised l = sum_j 2^(s_j log2(e) - R) (the page normalises the
  *     softmax before quantising p); the chunk's output N / (448 l) and
@@ -627,6 +630,8 @@ int oracle_decode_fp8(const float *q, const unsigned char *k8, const unsigned ch
  * ceil(S_max/32)] scales; o:[B,H,dc]; lse:[B,H].  split and tile are
  * positive multiples of 32, tile divides split.
  */
+#define MLA_FP8_HEADROOM 3.0
+
 int oracle_mla_decode_fp8(const float *q, const unsigned char *c8, const float *cs,
                           const int *seq_lens, double *o, double *lse,
                           int B, int S_max, int H, int dc, int dr, double scale,
@@ -635,6 +640,8 @@ int oracle_mla_decode_fp8(const float *q, const unsigned char *c8, const float *
     if (B < 0 || S_max < 0 || H <= 0 || dc <= 0 || dr < 0 || split <= 0 || tile <= 0 ||
         split % 32 || tile % 32 || split % tile) return -1;
     const int dk = dc + dr;
+    double val[256];                   /* fp8_value of every code, looked up below */
+    for (int c = 0; c < 256; ++c) val[c] = fp8_value((unsigned)c);
     const long nt = (S_max + 31) / 32;
     const long units = (long)B * H;
     const double log2e = 1.0 / log(2.0);
@@ -666,23 +673,24 @@ int oracle_mla_decode_fp8(const float *q, const unsigned char *c8, const float *
                         const unsigned char *row = c8 + ((size_t)b * S_max + j) * dk;
                         const double sc = (double)cs[b * nt + j / 32];
                         double acc = 0.0;
-                        for (int d = 0; d < dk; ++d) acc += fp8_value(q8[d]) * fp8_value(row[d]);
+                        for (int d = 0; d < dk; ++d) acc += val[q8[d]] * val[row[d]];
                         sn[j - t0] = scale * sq * sc * acc;
                         y[j - t0] = sn[j - t0] * log2e + log2(sc);
                         if (y[j - t0] > tmax) tmax = y[j - t0];
                     }
                     if (tmax > R) {                 /* move the reference, rescale */
-                        const double f = R == -INFINITY ? 0.0 : exp2(R - tmax);
+                        const double Rn = tmax + MLA_FP8_HEADROOM;
+                        const double f = R == -INFINITY ? 0.0 : exp2(R - Rn);
                         for (int d = 0; d < dc; ++d) num[d] *= f;
                         l *= f;
-                        R = tmax;
+                        R = Rn;
                     }
                     for (long j = t0; j < t1; ++j) {
                         const unsigned char *row = c8 + ((size_t)b * S_max + j) * dk;
                         double w = 448.0 * exp2(y[j - t0] - R);
                         if (w > 448.0) w = 448.0;
-                        const double pq = fp8_value(fp8_encode((float)w));
-                        for (int d = 0; d < dc; ++d) num[d] += pq * fp8_value(row[d]);
+                        const double pq = val[fp8_encode((float)w)];
+                        for (int d = 0; d < dc; ++d) num[d] += pq * val[row[d]];
                         l += exp2(sn[j - t0] * log2e - R);
                     }
                 }

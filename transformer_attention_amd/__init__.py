@@ -45,7 +45,7 @@ EXPORTED_SYMBOLS = (
     "mla_decode", "mla_decode_workspace_size", "attn_decode_paged",
     "attn_decode_paged_workspace_size", "mla_decode_paged", "mla_decode_paged_workspace_size",
     "attn_quantize_kv_fp8", "attn_decode_fp8", "attn_decode_paged_fp8", "attn_rope_qk",
-    "attn_decode_noalloc",
+    "attn_decode_noalloc", "mla_decode_fp8", "mla_decode_fp8_workspace_size",
     "attn_status_string",
     "attn_abi_version",
 )
@@ -101,6 +101,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P,
                                           I, P, Z, P]
     lib.attn_decode_paged_fp8.restype = I
+    lib.mla_decode_fp8_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.mla_decode_fp8_workspace_size.restype = Z
+    lib.mla_decode_fp8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, P, I, P, Z, P]
+    lib.mla_decode_fp8.restype = I
     lib.attn_decode_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, P, I, P]
     lib.attn_decode_noalloc.restype = I
     lib.attn_rope_qk.argtypes = [P, P, P, I, I, I, I, I, I, I, I, F, I, P]
@@ -374,6 +378,50 @@ def mla_decode(q, kv_cache, seq_lens, *, d_c: int = 512, d_r: int = 64, scale: f
                         B, S_max, H, d_c, d_r, float(scale), _ptr(sinks), int(split_tokens),
                         _ptr(workspace), ws_bytes, _stream(q.device))
     _check(st, "mla_decode")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def mla_decode_fp8_workspace_size(B, S_max, h_q, d_c=512, d_r=64, split_tokens=0) -> int:
+    return int(load_library().mla_decode_fp8_workspace_size(B, S_max, h_q, d_c, d_r,
+                                                            split_tokens))
+
+
+def mla_decode_fp8(q, kv_codes, kv_scales, seq_lens, *, d_c: int = 512, d_r: int = 64,
+                   scale: float, sinks=None, split_tokens: int = 0, o=None, lse=None,
+                   workspace=None, return_lse: bool = False):
+    """MLA decode with FP8 attention.  q:[B,H,d_c+d_r] bf16 (quantised in the
+    call); kv_codes:[B,S_max,d_c+d_r] uint8 E4M3; kv_scales:[B,ceil(S_max/32)]
+    fp32 (attn_quantize_kv_fp8 of the cache viewed as [B,1,S_max,d_c+d_r]);
+    seq_lens int32[B].  Returns o:[B,H,d_c] bf16."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16, ndim=3)
+    _require(kv_codes, "kv_codes", torch.uint8, q.device, 3)
+    _require(kv_scales, "kv_scales", torch.float32, q.device)
+    _require(seq_lens, "seq_lens", torch.int32, q.device, 1)
+    B, H, dk = q.shape
+    if dk != d_c + d_r or kv_codes.shape[0] != B or kv_codes.shape[2] != dk:
+        raise ValueError("q / kv_codes shape mismatch")
+    S_max = kv_codes.shape[1]
+    if kv_scales.numel() != B * ((S_max + 31) // 32):
+        raise ValueError("kv_scales must hold [B, ceil(S_max/32)] values")
+    if seq_lens.shape[0] != B:
+        raise ValueError("seq_lens shape mismatch")
+    if o is None:
+        o = torch.empty((B, H, d_c), dtype=torch.bfloat16, device=q.device)
+    _require(o, "o", torch.bfloat16, q.device)
+    if o.numel() != B * H * d_c:
+        raise ValueError("o shape mismatch")
+    lse = _lse_out(lse, B, H, q.device, return_lse)
+    need = lib.mla_decode_fp8_workspace_size(B, S_max, H, d_c, d_r, int(split_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", None, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.mla_decode_fp8(_ptr(q), _ptr(kv_codes), _ptr(kv_scales), _ptr(o), _ptr(lse),
+                            _ptr(seq_lens), B, S_max, H, d_c, d_r, float(scale),
+                            _ptr(_sinks(sinks, H, q.device)), int(split_tokens), _ptr(workspace),
+                            ws_bytes, _stream(q.device))
+    _check(st, "mla_decode_fp8")
     return (o, lse) if (return_lse or lse is not None) else o
 
 

@@ -346,6 +346,42 @@ attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *ls
     return mi355::launch_mla_decode_bf16(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+size_t mla_decode_fp8_workspace_size(int B, int S_max, int h_q, int d_c, int d_r, int split_tokens) {
+    const size_t base = mla_decode_workspace_size(B, S_max, h_q, d_c, d_r, split_tokens);
+    if (base == 0) return 0;
+    const size_t rows = (size_t)B * h_q;
+    return base + align_up(rows * (size_t)(d_c + d_r), 256) + align_up(rows * sizeof(float), 256);
+}
+
+attn_status_t mla_decode_fp8(const void *q, const void *kv_codes, const float *kv_scales, void *o,
+                             float *lse, const int32_t *seq_lens, int B, int S_max, int h_q,
+                             int d_c, int d_r, float scale, const float *sinks, int split_tokens,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (bad_ptr(q) || bad_ptr(kv_codes) || bad_ptr(kv_scales) || bad_ptr(o) || bad_ptr(seq_lens))
+        return ATTN_ERR_INVALID_ARG;
+    if (B <= 0 || S_max <= 0 || h_q <= 0 || d_c <= 0 || d_r < 0) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f) || split_tokens < 0 || split_tokens % 64)
+        return ATTN_ERR_INVALID_ARG;
+    if (d_c != 512 || d_r != 64) return ATTN_ERR_UNSUPPORTED;
+    if (B > 65535 || (long long)B * h_q * (d_c + d_r) >= (1LL << 40)) return ATTN_ERR_UNSUPPORTED;
+    const int split = split_tokens ? split_tokens : default_mla_split(B, S_max, h_q);
+    const int ns = (S_max + split - 1) / split;
+    const size_t need = mla_decode_fp8_workspace_size(B, S_max, h_q, d_c, d_r, split_tokens);
+    if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    char *w = static_cast<char *>(workspace);
+    const size_t rows = (size_t)B * h_q;
+    float *ws_o = reinterpret_cast<float *>(w);
+    w += align_up(rows * ns * d_c * sizeof(float), 256);
+    float *ws_lse = reinterpret_cast<float *>(w);
+    w += align_up(rows * ns * sizeof(float), 256);
+    void *ws_q8 = w;
+    w += align_up(rows * (size_t)(d_c + d_r), 256);
+    float *ws_qs = reinterpret_cast<float *>(w);
+    mi355::MlaFp8Args a{q, kv_codes, kv_scales, o, lse, seq_lens, B, S_max, h_q, scale, split, ns,
+                        ws_o, ws_lse, ws_q8, ws_qs, sinks};
+    return mi355::launch_mla_decode_fp8(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 size_t mla_decode_paged_workspace_size(int B, int max_blocks, int page_size, int h_q, int d_c,
                                        int d_r, int split_tokens) {
     if (max_blocks <= 0 || page_size <= 0 || (long long)max_blocks * page_size > 0x7fffffffLL) return 0;

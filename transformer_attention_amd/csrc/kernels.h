@@ -90,6 +90,26 @@ struct MlaArgs {
 };
 hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream);
 
+// MLA decode with FP8 attention: the cache as E4M3 codes [B, S_max, d_c + d_r]
+// with one fp32 scale per 32 tokens [B, ceil(S_max / 32)]; the bf16 query is
+// quantised per head into ws_q8 / ws_qs first.
+struct MlaFp8Args {
+    const void *q;              // [B, H, d_c + d_r] bf16
+    const void *cache;          // codes
+    const float *cache_scales;
+    void *o;
+    float *lse;
+    const int32_t *seq_lens;
+    int B, S_max, H;
+    float scale;
+    int split, n_split_max;     // split: a multiple of 64
+    float *ws_o, *ws_lse;       // as MlaArgs
+    void *ws_q8;                // [B, H, d_c + d_r] query codes
+    float *ws_qs;               // [B, H] query scales
+    const float *sinks;
+};
+hipError_t launch_mla_decode_fp8(const MlaFp8Args &a, hipStream_t stream);
+
 // Rotary position embedding of q [B, hq, T, row_q] and k [B, hk, T, row_k]
 // (k may be null with hk = 0), dimensions [rope_offset, rope_offset +
 // rope_dim) of each row, in place.
