@@ -712,6 +712,104 @@ int oracle_mla_decode_fp8(const float *q, const unsigned char *c8, const float *
 }
 
 /*
+ * Prefill with FP8 attention: the pages' FP8 recipe ("Flash Attention 3 and
+ * Multi-Headed Latent Attention", the FP8 attention section: q, k and v
+ * quantised to E4M3 per tile with scale amax / 448, both products on FP8
+ * operands, p quantised before the second) on the prefill forward above,
+ * with the steps and readings of oracle_mla_decode_fp8:
+ *  - q, k and v arrive as codes with one scale per 32 positions of a head
+ *    (the cache quantiser's tiles): qs[b,h,i/32], ks / vs[b,g,j/32];
+ *  - s_ij = scale * qs_i * ks_j * (q8_i . k8_j) (exact dequantised product);
+ *  - the weight of key j carries its value scale: y_ij = s_ij log2(e) +
+ *    log2(vs_j);
+ *  - row i takes its visible keys in tiles of `tile` keys aligned at
+ *    multiples of `tile`, in increasing order; its reference R (-inf at the
+ *    start) moves to a tile's max of y plus MLA_FP8_HEADROOM when the tile
+ *    exceeds it, rescaling what was accumulated by 2^(R_old - R_new);
+ *  - P8_ij = E4M3(min(448, 448 * 2^(y_ij - R))); numerator sum_j P8_ij v8_j,
+ *    unquantised denominator l = sum_j 2^(s_ij log2(e) - R); o = num / (448
+ *    l), lse = (R + log2 l) ln 2; a sink logit joins as in the plain prefill.
+ * q8:[B,hq,T,d] qs:[B,hq,ceil(T/32)]  k8,v8:[B,hkv,T,d] ks,vs:[B,hkv,ceil(T/32)]
+ * o:[B,hq,T,d]  lse:[B,hq,T] (may be NULL).
+ */
+int oracle_prefill_fp8(const unsigned char *q8, const float *qs, const unsigned char *k8,
+                       const float *ks, const unsigned char *v8, const float *vs,
+                       double *o, double *lse, int B, int T, int hq, int hkv, int d,
+                       int causal, int window, double scale, const float *sinks, int tile)
+{
+    if (B < 0 || T < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv || tile <= 0 || tile % 32)
+        return -1;
+    const int G = hq / hkv;
+    const long nt = (T + 31) / 32;
+    const long rows = (long)B * hq * T;
+    const double log2e = 1.0 / log(2.0);
+    double val[256];
+    for (int c = 0; c < 256; ++c) val[c] = fp8_value((unsigned)c);
+#pragma omp parallel
+    {
+        double *num = (double *)malloc(sizeof(double) * d);
+        double *sn = (double *)malloc(sizeof(double) * tile);
+        double *y = (double *)malloc(sizeof(double) * tile);
+        unsigned char *vis = (unsigned char *)malloc(tile);
+#pragma omp for schedule(dynamic, 16)
+        for (long u = 0; u < rows; ++u) {
+            const long i = u % T, h = (u / T) % hq, b = u / ((long)T * hq);
+            const long g = h / G, bg = b * hkv + g;
+            const unsigned char *qi = q8 + u * d;
+            const double sq = (double)qs[(b * hq + h) * nt + i / 32];
+            double R = -INFINITY, l = 0.0;
+            for (int e = 0; e < d; ++e) num[e] = 0.0;
+            for (long t0 = 0; t0 < T; t0 += tile) {
+                double tmax = -INFINITY;
+                int any = 0;
+                for (long j = t0; j < t0 + tile; ++j) {
+                    vis[j - t0] = (unsigned char)(j < T && prefill_visible(i, j, causal, window));
+                    if (!vis[j - t0]) continue;
+                    any = 1;
+                    const unsigned char *kj = k8 + (bg * (long)T + j) * d;
+                    double acc = 0.0;
+                    for (int e = 0; e < d; ++e) acc += val[qi[e]] * val[kj[e]];
+                    sn[j - t0] = scale * sq * (double)ks[bg * nt + j / 32] * acc;
+                    y[j - t0] = sn[j - t0] * log2e + log2((double)vs[bg * nt + j / 32]);
+                    if (y[j - t0] > tmax) tmax = y[j - t0];
+                }
+                if (!any) continue;
+                if (tmax > R) {
+                    const double Rn = tmax + MLA_FP8_HEADROOM;
+                    const double f = R == -INFINITY ? 0.0 : exp2(R - Rn);
+                    for (int e = 0; e < d; ++e) num[e] *= f;
+                    l *= f;
+                    R = Rn;
+                }
+                for (long j = t0; j < t0 + tile; ++j) {
+                    if (!vis[j - t0]) continue;
+                    double w = 448.0 * exp2(y[j - t0] - R);
+                    if (w > 448.0) w = 448.0;
+                    const double pq = val[fp8_encode((float)w)];
+                    const unsigned char *vj = v8 + (bg * (long)T + j) * d;
+                    for (int e = 0; e < d; ++e) num[e] += pq * val[vj[e]];
+                    l += exp2(sn[j - t0] * log2e - R);
+                }
+            }
+            double *orow = o + u * d;
+            double L = l > 0.0 ? (R + log2(l)) * log(2.0) : -INFINITY;
+            for (int e = 0; e < d; ++e) orow[e] = l > 0.0 ? num[e] / (448.0 * l) : 0.0;
+            if (sinks && sinks[h] != -INFINITY) {       /* merge with the sink's empty part */
+                const double sk = (double)sinks[h];
+                const double M = L > sk ? L : sk;
+                const double Ln = M + log(exp(L - M) + exp(sk - M));
+                const double f = L == -INFINITY ? 0.0 : exp(L - Ln);
+                for (int e = 0; e < d; ++e) orow[e] *= f;
+                L = Ln;
+            }
+            if (lse) lse[u] = L;
+        }
+        free(num); free(sn); free(y); free(vis);
+    }
+    return 0;
+}
+
+/*
  * Rotary position embedding ("Attention Engineering: From MHA to GQA, MLA &
  * FlashAttention", section 1, the complex-plane derivation and the
  * relative-distance identity): the rotated dimensions of a row are taken in

@@ -144,3 +144,104 @@ def test_empty_sequence(oracle_mod):
     o, l = oracle_mod.mla_decode_fp8(q, codes[:, 0], scales[:, 0], lens, d_c=DC, d_r=DR,
                                      scale=0.07, split=64, sinks=sk)
     assert np.all(o[0] == 0) and np.allclose(l[0], sk)
+
+
+# ---------------------------------------------------------------- prefill ---
+
+def _tile_exact(rng, rows, d, f, score_col=None, score_vals=None):
+    """rows x d values on the E4M3 grid times f (a power of two), with the
+    amax 448 f at [0, 5] so the tile's scale is exactly f."""
+    grid = np.array(list(np.arange(0, 16) / 8.0) + [2.0, 3.0, 4.0, 6.0, 8.0])
+    vals = rng.choice(grid, size=(rows, d)) * rng.choice([-1.0, 1.0], size=(rows, d))
+    vals[0, 5] = 448.0
+    if score_col is not None:
+        vals[:, 0] = 0.0
+        vals[:, score_col] = score_vals / f
+    return (vals * f).astype(np.float32)
+
+
+def _exact_prefill_case(rng, B, T, hq, hkv, d):
+    # q: per row amax 7 at e = 0 (scale 7 / 448 = 2^-6 exactly), 1 at e = 1,
+    # zero elsewhere, so a score is exactly k[1] times the scale
+    q = np.zeros((B, hq, T, d), np.float32)
+    q[..., 0] = 7.0
+    q[..., 1] = 1.0
+    k = np.zeros((B, hkv, T, d), np.float32)
+    v = np.zeros((B, hkv, T, d), np.float32)
+    for b in range(B):
+        for g in range(hkv):
+            for t in range((T + 31) // 32):
+                r0, r1 = 32 * t, min(T, 32 * t + 32)
+                fk = 2.0 ** [0, -1, 1][(b + g + t) % 3]
+                fv = 2.0 ** [1, 0, -1][(b + 2 * g + t) % 3]
+                m = rng.integers(-1, 2, size=r1 - r0) * 4.0          # k . q = 4m: integer log2 weights
+                k[b, g, r0:r1] = _tile_exact(rng, r1 - r0, d, fk, score_col=1, score_vals=m)
+                v[b, g, r0:r1] = _tile_exact(rng, r1 - r0, d, fv)
+    return q, k, v
+
+
+@pytest.mark.parametrize("causal,window,tile", [(True, 0, 64), (True, 40, 64), (False, 0, 32),
+                                                (True, 0, 128)])
+def test_prefill_fp8_exact_case_is_the_plain_prefill(oracle_mod, causal, window, tile):
+    rng = np.random.default_rng(41)
+    B, T, hq, hkv, d = 2, 150, 4, 2, 16
+    q, k, v = _exact_prefill_case(rng, B, T, hq, hkv, d)
+    q8, qs = oracle_mod.quantize_kv_fp8(q)
+    k8, ks = oracle_mod.quantize_kv_fp8(k)
+    v8, vs = oracle_mod.quantize_kv_fp8(v)
+    for x8, xs, x in ((q8, qs, q), (k8, ks, k), (v8, vs, v)):      # the construction is exact
+        assert np.array_equal(oracle_mod.fp8_dequantize(x8, xs), x)
+    sinks = np.array([0.3, -2.0, 1.5, 0.0], np.float32)
+    for sk in (None, sinks):
+        o8, l8 = oracle_mod.prefill_fp8(q8, qs, k8, ks, v8, vs, causal=causal, window=window,
+                                        scale=math.log(2.0), tile=tile, sinks=sk)
+        o, l = oracle_mod.prefill(q, k, v, causal=causal, window=window, scale=math.log(2.0),
+                                  sinks=sk)
+        assert np.abs(o8 - o).max() <= 1e-12 * max(1.0, np.abs(o).max())
+        assert np.abs(l8 - l).max() <= 1e-12 * max(1.0, np.abs(l).max())
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 70), (False, 0)])
+def test_prefill_fp8_weight_rounding_within_the_e4m3_step(oracle_mod, causal, window):
+    rng = np.random.default_rng(42)
+    B, T, hq, hkv, d = 1, 300, 4, 2, 64
+    q = rng.standard_normal((B, hq, T, d)).astype(np.float32)
+    k = rng.standard_normal((B, hkv, T, d)).astype(np.float32)
+    v = (rng.standard_normal((B, hkv, T, d)) * rng.uniform(0.3, 3, (B, hkv, T, 1))).astype(np.float32)
+    q8, qs = oracle_mod.quantize_kv_fp8(q)
+    k8, ks = oracle_mod.quantize_kv_fp8(k)
+    v8, vs = oracle_mod.quantize_kv_fp8(v)
+    qd, kd, vd = (oracle_mod.fp8_dequantize(a, s) for a, s in ((q8, qs), (k8, ks), (v8, vs)))
+    scale = 1.0 / math.sqrt(d)
+    o8, l8 = oracle_mod.prefill_fp8(q8, qs, k8, ks, v8, vs, causal=causal, window=window,
+                                    scale=scale)
+    oq, lq = oracle_mod.prefill(qd, kd, vd, causal=causal, window=window, scale=scale)
+    assert np.abs(o8 - oq).max() <= np.abs(vd).max() / 16.0
+    assert np.abs(l8 - lq).max() < 1e-5
+    rel = np.linalg.norm(o8 - oq) / np.linalg.norm(oq)
+    assert 1e-4 < rel < 5e-2
+    o, _ = oracle_mod.prefill(q, k, v, causal=causal, window=window, scale=scale)
+    assert np.linalg.norm(o8 - o) / np.linalg.norm(o) < 0.15
+
+
+def test_prefill_fp8_masked_keys_are_excluded(oracle_mod):
+    rng = np.random.default_rng(43)
+    B, T, hq, hkv, d = 1, 130, 2, 1, 32
+    q = rng.standard_normal((B, hq, T, d)).astype(np.float32)
+    k = rng.standard_normal((B, hkv, T, d)).astype(np.float32)
+    v = rng.standard_normal((B, hkv, T, d)).astype(np.float32)
+    q8, qs = oracle_mod.quantize_kv_fp8(q)
+    k8, ks = oracle_mod.quantize_kv_fp8(k)
+    v8, vs = oracle_mod.quantize_kv_fp8(v)
+    a = oracle_mod.prefill_fp8(q8, qs, k8, ks, v8, vs, causal=True, window=20, scale=0.2)
+    cut = 70
+    kp, vp = k8.copy(), v8.copy()
+    kp[:, :, cut:] = 0x7f
+    vp[:, :, cut:] = 0xff
+    b_ = oracle_mod.prefill_fp8(q8, qs, kp, ks, vp, vs, causal=True, window=20, scale=0.2)
+    assert np.array_equal(a[0][:, :, :cut], b_[0][:, :, :cut])
+    kp, vp = k8.copy(), v8.copy()
+    kp[:, :, :30] = 0x7f                             # outside the window of rows >= 49
+    vp[:, :, :30] = 0xff
+    c_ = oracle_mod.prefill_fp8(q8, qs, kp, ks, vp, vs, causal=True, window=20, scale=0.2)
+    assert np.array_equal(a[0][:, :, 49:], c_[0][:, :, 49:])
