@@ -294,6 +294,28 @@ def bench_mla_fp8(torch, ta, W, steps, warmup, copies=3):
             "cache_copies_rotated": copies}
 
 
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 (E4M3) MFMA, TFLOP/s
+
+
+def bench_prefill_fp8(torch, ta, W, shape, steps, warmup):
+    """The Llama-3-8B-shaped causal prefill with FP8 attention: q, k and v
+    quantised to E4M3 (one scale per 32 positions of a head) by the
+    library's quantiser before timing."""
+    q, k, v = W.prefill_inputs(shape, seed=0, device="cuda", gen_device="cuda")
+    (q8, qs), (k8, ks), (v8, vs) = (ta.attn_quantize_kv_fp8(x) for x in (q, k, v))
+    del q, k, v
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = lambda: ta.attn_prefill_fp8(q8, k8, v8, qs, ks, vs, causal=shape.causal,
+                                     window=shape.window, scale=shape.scale, o=o)
+    ms, wall = _events_time(torch, fn, steps, warmup, stream, key="prefill_fp8")
+    flops = prefill_flops(shape)
+    tflops = flops / (ms * 1e-3) / 1e12
+    del q8, k8, v8, qs, ks, vs, o
+    return {"ms": ms, "wall_s": wall, "flops": flops, "tflops": tflops,
+            "frac_fp8_peak": tflops / FP8_PEAK_TFLOPS}
+
+
 def bench_tiny_fp32(torch, ta, W, steps, warmup):
     """The tiny fp32 causal GQA prefill (B=1, T=64, 4/2 heads, d_h=16): a
     parity case whose time is one kernel launch; reported in microseconds."""
@@ -367,8 +389,8 @@ def _library_info(ta):
             "sha256_16": digest[:16]}
 
 
-BENCHES = ("prefill", "swa-mha", "swa-mqa", "backward", "decode", "decode-fp8", "rope",
-           "decode-paged", "mla", "mla-fp8", "tiny-fp32", "copy")
+BENCHES = ("prefill", "swa-mha", "swa-mqa", "backward", "prefill-fp8", "decode", "decode-fp8",
+           "rope", "decode-paged", "mla", "mla-fp8", "tiny-fp32", "copy")
 
 
 def main(argv=None):
@@ -402,6 +424,7 @@ def main(argv=None):
         "swa-mha": lambda: bench_prefill(torch, ta, W, W.SWA_MHA, steps, warmup),
         "swa-mqa": lambda: bench_prefill(torch, ta, W, W.SWA_MQA, steps, warmup),
         "backward": lambda: bench_backward(torch, ta, W, shape, steps, warmup),
+        "prefill-fp8": lambda: bench_prefill_fp8(torch, ta, W, shape, steps, warmup),
         "decode": lambda: bench_decode(torch, ta, W, steps, warmup),
         "decode-fp8": lambda: bench_decode_fp8(torch, ta, W, steps, warmup),
         "rope": lambda: bench_rope(torch, ta, W, steps, warmup),
@@ -473,6 +496,8 @@ def main(argv=None):
         elif "frac_bf16_peak" in d:
             o.update({"TFLOP_s": round(d["tflops"], 2),
                       "frac_bf16_peak": round(d["frac_bf16_peak"], 4), "flops": d["flops"]})
+        elif "tflops" in d:
+            o.update({"TFLOP_s": round(d["tflops"], 2), "flops": d["flops"]})
         o.update(extra)
         line[key.replace("-", "_")] = o
 
@@ -480,6 +505,9 @@ def main(argv=None):
         "swa-mha": "sliding-window MHA prefill, B=4, T=4096, 32/32 heads, W=1024",
         "swa-mqa": "sliding-window MQA prefill, B=4, T=4096, 32/1 heads, W=1024",
         "backward": "Llama-3-8B-shaped causal GQA prefill backward (dQ, dK, dV)",
+        "prefill-fp8": "Llama-3-8B-shaped causal GQA prefill with FP8 attention (E4M3 q, k, v "
+                       "with one scale per 32 positions of a head, p quantised in the kernel, "
+                       "FP8 MFMA); lower precision, not the bf16 workload",
         "decode": "70B-shaped GQA decode, B=64, 64/8 heads, S_max=32768",
         "decode-fp8": "70B-shaped GQA decode, cache in FP8 E4M3 (one scale per 32 positions of "
                       "a head)",
@@ -511,6 +539,11 @@ def main(argv=None):
         if key in ("mla", "mla-fp8"):
             extra.update({"TFLOP_s": round(out[key]["tflops"], 2),
                           "cache_copies_rotated": out[key]["cache_copies_rotated"]})
+        if key == "prefill-fp8":
+            extra.update({"dtype": "fp8 e4m3 operands, fp32 accumulate",
+                          "frac_fp8_peak": round(out[key]["frac_fp8_peak"], 4)})
+            if "prefill" in out:
+                extra["speedup_vs_bf16"] = round(out["prefill"]["ms"] / out[key]["ms"], 3)
         if key == "mla-fp8":
             extra["dtype"] = "fp8 e4m3 operands, fp32 accumulate"
             if "mla" in out:

@@ -97,6 +97,37 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
                            const float *sinks, hipStream_t stream);
 
 /*
+ * attn_prefill_fp8 -- attn_prefill with FP8 attention: the pages' FP8 recipe
+ * ("Flash Attention 3 and Multi-Headed Latent Attention", the FP8 attention
+ * section: q, k and v quantised to E4M3 per tile with scale amax / 448,
+ * both matrix products on FP8 operands, p quantised before the second,
+ * results dequantised by the scales), both products on E4M3 matrix
+ * instructions with fp32 accumulation.
+ *
+ *   q        : [B, h_q,  T, d_h] uint8 E4M3 codes   (read)
+ *   k, v     : [B, h_kv, T, d_h] uint8 E4M3 codes   (read)
+ *   q_scales : [B, h_q,  ceil(T / 32)] float32      (read)
+ *   k_scales, v_scales : [B, h_kv, ceil(T / 32)] float32 (read)
+ *              one scale per 32 positions of a head: the layout
+ *              attn_quantize_kv_fp8 writes for each of q, k and v
+ *   o        : [B, h_q, T, d_h] bf16 (written);  lse : [B, h_q, T] or NULL
+ * s_ij = scale * sq_i * sk_j * (q8_i . k8_j).  Each row's probabilities are
+ * quantised to E4M3 in 64-key tiles against the row's reference R, with the
+ * value scale of their key folded in: e = 448 * 2^(y - R), y = s log2(e) +
+ * log2(sv_j); when a tile's max of y exceeds R, R moves to that max plus 3
+ * (log2 units), so no weight passes 448.  o = sum_j e_j v8_j / (448 l), l =
+ * sum_j 2^(s_ij log2(e) - R) unquantised; lse = (R + log2 l) ln 2.  causal,
+ * window, scale and sinks as for attn_prefill; masked keys inside a visited
+ * tile must have finite codes (not 0x7f / 0xff).  Supported: d_h = 128.
+ */
+attn_status_t attn_prefill_fp8(const void *q, const void *k, const void *v,
+                               const float *q_scales, const float *k_scales,
+                               const float *v_scales, void *o, float *lse,
+                               int B, int T, int h_q, int h_kv, int d_h, int causal,
+                               int window, float scale, const float *sinks,
+                               hipStream_t stream);
+
+/*
  * attn_prefill_backward -- gradients of attn_prefill with respect to q, k, v.
  *
  *   q, o, dout : [B, h_q,  T, d_h]  dtype    (read; o and lse are what

@@ -81,7 +81,7 @@ def _load():
     lib.oracle_decode_fp8.restype = I
     lib.oracle_mla_decode_fp8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, D, P, I, I]
     lib.oracle_mla_decode_fp8.restype = I
-    lib.oracle_prefill_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, P, I]
+    lib.oracle_prefill_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, P, I, P, I]
     lib.oracle_prefill_fp8.restype = I
     lib.oracle_rope.argtypes = [P, P, P, I, I, I, I, I, I, D]
     lib.oracle_rope.restype = I
@@ -355,7 +355,7 @@ def mla_decode_fp8(q, codes, scales, seq_lens, *, d_c: int, d_r: int, scale: flo
 
 
 def prefill_fp8(q8, q_scales, k8, k_scales, v8, v_scales, *, causal: bool, window: int = 0,
-                scale: float, tile: int = 64, sinks=None):
+                scale: float, tile: int = 64, sinks=None, rows=None):
     """Prefill with FP8 attention (the pages' FA3 FP8 recipe): q, k, v as
     E4M3 codes [B,h,T,d] with one scale per 32 positions of a head
     [B,h,ceil(T/32)] (the cache quantiser's layout), both products on the
@@ -363,7 +363,8 @@ def prefill_fp8(q8, q_scales, k8, k_scales, v8, v_scales, *, causal: bool, windo
     its reference (keys in ``tile``-aligned tiles; the reference moves to a
     tile's max plus 3, log2 units, when the tile exceeds it) with the value
     scale folded in, the denominator from the unquantised probabilities.
-    Returns (o:[B,hq,T,d], lse:[B,hq,T])."""
+    ``rows`` optionally lists the query positions to evaluate.  Returns
+    (o:[B,hq,n_rows,d], lse:[B,hq,n_rows])."""
     q8 = np.ascontiguousarray(np.asarray(q8, dtype=np.uint8))
     k8 = np.ascontiguousarray(np.asarray(k8, dtype=np.uint8))
     v8 = np.ascontiguousarray(np.asarray(v8, dtype=np.uint8))
@@ -373,12 +374,20 @@ def prefill_fp8(q8, q_scales, k8, k_scales, v8, v_scales, *, causal: bool, windo
     nt = (T + 31) // 32
     qs, ks, vs = (_f32(x).reshape(-1) for x in (q_scales, k_scales, v_scales))
     assert qs.size == B * hq * nt and ks.size == B * hkv * nt and vs.size == ks.size
-    o = np.zeros((B, hq, T, d), dtype=np.float64)
-    lse = np.zeros((B, hq, T), dtype=np.float64)
+    if rows is None:
+        rows_arr, n_rows, rows_ptr = None, T, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        assert rows_arr.ndim == 1 and (rows_arr.size == 0 or (
+            rows_arr.min() >= 0 and rows_arr.max() < T))
+        n_rows, rows_ptr = int(rows_arr.size), _ptr(rows_arr)
+    o = np.zeros((B, hq, n_rows, d), dtype=np.float64)
+    lse = np.zeros((B, hq, n_rows), dtype=np.float64)
     sk, sk_ptr = _sinks(sinks, hq)
     rc = _load().oracle_prefill_fp8(_ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(v8), _ptr(vs),
                                     _ptr(o), _ptr(lse), B, T, hq, hkv, d, int(bool(causal)),
-                                    int(window), float(scale), sk_ptr, int(tile))
+                                    int(window), float(scale), sk_ptr, int(tile), rows_ptr,
+                                    n_rows)
     if rc != 0:
         raise ValueError("oracle_prefill_fp8: invalid shape")
     return o, lse

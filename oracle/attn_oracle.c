@@ -730,18 +730,21 @@ int oracle_mla_decode_fp8(const float *q, const unsigned char *c8, const float *
  *    unquantised denominator l = sum_j 2^(s_ij log2(e) - R); o = num / (448
  *    l), lse = (R + log2 l) ln 2; a sink logit joins as in the plain prefill.
  * q8:[B,hq,T,d] qs:[B,hq,ceil(T/32)]  k8,v8:[B,hkv,T,d] ks,vs:[B,hkv,ceil(T/32)]
- * o:[B,hq,T,d]  lse:[B,hq,T] (may be NULL).
+ * row_list: optional n_rows query positions (NULL = all T, in order);
+ * o:[B,hq,n_rows,d]  lse:[B,hq,n_rows] (may be NULL).
  */
 int oracle_prefill_fp8(const unsigned char *q8, const float *qs, const unsigned char *k8,
                        const float *ks, const unsigned char *v8, const float *vs,
                        double *o, double *lse, int B, int T, int hq, int hkv, int d,
-                       int causal, int window, double scale, const float *sinks, int tile)
+                       int causal, int window, double scale, const float *sinks, int tile,
+                       const int *row_list, int n_rows)
 {
     if (B < 0 || T < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv || tile <= 0 || tile % 32)
         return -1;
+    if (!row_list) n_rows = T;
     const int G = hq / hkv;
     const long nt = (T + 31) / 32;
-    const long rows = (long)B * hq * T;
+    const long rows = (long)B * hq * n_rows;
     const double log2e = 1.0 / log(2.0);
     double val[256];
     for (int c = 0; c < 256; ++c) val[c] = fp8_value((unsigned)c);
@@ -753,9 +756,10 @@ int oracle_prefill_fp8(const unsigned char *q8, const float *qs, const unsigned 
         unsigned char *vis = (unsigned char *)malloc(tile);
 #pragma omp for schedule(dynamic, 16)
         for (long u = 0; u < rows; ++u) {
-            const long i = u % T, h = (u / T) % hq, b = u / ((long)T * hq);
+            const long r = u % n_rows, h = (u / n_rows) % hq, b = u / ((long)n_rows * hq);
+            const long i = row_list ? row_list[r] : r;
             const long g = h / G, bg = b * hkv + g;
-            const unsigned char *qi = q8 + u * d;
+            const unsigned char *qi = q8 + (((b * hq + h) * (long)T) + i) * d;
             const double sq = (double)qs[(b * hq + h) * nt + i / 32];
             double R = -INFINITY, l = 0.0;
             for (int e = 0; e < d; ++e) num[e] = 0.0;

@@ -245,3 +245,15 @@ def test_prefill_fp8_masked_keys_are_excluded(oracle_mod):
     vp[:, :, :30] = 0xff
     c_ = oracle_mod.prefill_fp8(q8, qs, kp, ks, vp, vs, causal=True, window=20, scale=0.2)
     assert np.array_equal(a[0][:, :, 49:], c_[0][:, :, 49:])
+
+
+def test_prefill_fp8_selected_rows_equal_the_full_result(oracle_mod):
+    rng = np.random.default_rng(44)
+    B, T, hq, hkv, d = 2, 140, 4, 2, 32
+    x = [rng.standard_normal((B, h, T, d)).astype(np.float32) for h in (hq, hkv, hkv)]
+    (q8, qs), (k8, ks), (v8, vs) = (oracle_mod.quantize_kv_fp8(a) for a in x)
+    o, l = oracle_mod.prefill_fp8(q8, qs, k8, ks, v8, vs, causal=True, window=50, scale=0.17)
+    rows = [0, 5, 63, 64, 99, 139]
+    o2, l2 = oracle_mod.prefill_fp8(q8, qs, k8, ks, v8, vs, causal=True, window=50, scale=0.17,
+                                    rows=rows)
+    assert np.array_equal(o[:, :, rows], o2) and np.array_equal(l[:, :, rows], l2)

@@ -45,7 +45,7 @@ EXPORTED_SYMBOLS = (
     "mla_decode", "mla_decode_workspace_size", "attn_decode_paged",
     "attn_decode_paged_workspace_size", "mla_decode_paged", "mla_decode_paged_workspace_size",
     "attn_quantize_kv_fp8", "attn_decode_fp8", "attn_decode_paged_fp8", "attn_rope_qk",
-    "attn_decode_noalloc", "mla_decode_fp8", "mla_decode_fp8_workspace_size",
+    "attn_decode_noalloc", "mla_decode_fp8", "mla_decode_fp8_workspace_size", "attn_prefill_fp8",
     "attn_status_string",
     "attn_abi_version",
 )
@@ -101,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P,
                                           I, P, Z, P]
     lib.attn_decode_paged_fp8.restype = I
+    lib.attn_prefill_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P]
+    lib.attn_prefill_fp8.restype = I
     lib.mla_decode_fp8_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.mla_decode_fp8_workspace_size.restype = Z
     lib.mla_decode_fp8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, P, I, P, Z, P]
@@ -207,6 +209,47 @@ def attn_prefill(q, k, v, *, causal: bool = True, window: int = 0, scale=None,
                           hkv, d, _DT[q.dtype], int(bool(causal)), int(window),
                           float(scale), _ptr(sinks), _stream(q.device))
     _check(st, "attn_prefill")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_prefill_fp8(q8, k8, v8, q_scales, k_scales, v_scales, *, causal: bool = True,
+                     window: int = 0, scale=None, sinks=None, o=None, lse=None,
+                     return_lse: bool = False):
+    """Prefill with FP8 attention.  q8:[B,h_q,T,128], k8,v8:[B,h_kv,T,128] uint8
+    E4M3 codes; scales fp32 [B,h,ceil(T/32)] (attn_quantize_kv_fp8 of q, k, v).
+    Returns o:[B,h_q,T,128] bf16 (and lse when requested)."""
+    lib = load_library()
+    _require(q8, "q8", torch.uint8, ndim=4)
+    _require(k8, "k8", torch.uint8, q8.device, 4)
+    _require(v8, "v8", torch.uint8, q8.device, 4)
+    B, hq, T, d = q8.shape
+    hkv = k8.shape[1]
+    if tuple(k8.shape) != (B, hkv, T, d) or tuple(v8.shape) != (B, hkv, T, d):
+        raise ValueError("k8/v8 shape mismatch")
+    nt = (T + 31) // 32
+    for t, name, hh in ((q_scales, "q_scales", hq), (k_scales, "k_scales", hkv),
+                        (v_scales, "v_scales", hkv)):
+        _require(t, name, torch.float32, q8.device)
+        if t.numel() != B * hh * nt:
+            raise ValueError(f"{name} must hold [B, h, ceil(T/32)] values")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, hq, T, d), dtype=torch.bfloat16, device=q8.device)
+    _require(o, "o", torch.bfloat16, q8.device)
+    if o.numel() != B * hq * T * d:
+        raise ValueError("o shape mismatch")
+    if lse is None and return_lse:
+        lse = torch.empty((B, hq, T), dtype=torch.float32, device=q8.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, q8.device)
+        if lse.numel() != B * hq * T:
+            raise ValueError("lse shape mismatch")
+    st = lib.attn_prefill_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scales), _ptr(k_scales),
+                              _ptr(v_scales), _ptr(o), _ptr(lse), B, T, hq, hkv, d,
+                              int(bool(causal)), int(window), float(scale),
+                              _ptr(_sinks(sinks, hq, q8.device)), _stream(q8.device))
+    _check(st, "attn_prefill_fp8")
     return (o, lse) if (return_lse or lse is not None) else o
 
 

@@ -124,6 +124,24 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status_t attn_prefill_fp8(const void *q, const void *k, const void *v, const float *q_scales,
+                               const float *k_scales, const float *v_scales, void *o, float *lse,
+                               int B, int T, int h_q, int h_kv, int d_h, int causal, int window,
+                               float scale, const float *sinks, hipStream_t stream) {
+    if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(o) || bad_ptr(q_scales) ||
+        bad_ptr(k_scales) || bad_ptr(v_scales))
+        return ATTN_ERR_INVALID_ARG;
+    if (B <= 0 || T <= 0 || h_q <= 0 || h_kv <= 0 || d_h <= 0) return ATTN_ERR_INVALID_ARG;
+    if (h_q % h_kv != 0) return ATTN_ERR_INVALID_ARG;
+    if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+    if (d_h != 128) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * h_q * T * d_h >= (1LL << 40)) return ATTN_ERR_UNSUPPORTED;
+    mi355::PrefillFp8Args a{q, k, v, q_scales, k_scales, v_scales, o, lse, B, T, h_q, h_kv,
+                            causal ? 1 : 0, window, scale, sinks};
+    return mi355::launch_prefill_fp8_d128(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 size_t attn_prefill_backward_workspace_size(int B, int T, int h_q) {
     if (B <= 0 || T <= 0 || h_q <= 0) return 0;
     const long long tpad = ((long long)T + 63) / 64 * 64;

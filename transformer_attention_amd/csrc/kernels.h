@@ -28,6 +28,21 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs &a, hipStream_t stream);
 // fp32, d in {16, 32, 64, 128}, fp32 FMA.
 hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t stream);
 
+// Prefill with FP8 attention, d = 128: q, k, v as E4M3 codes ([B, hq, T, d]
+// and [B, hkv, T, d]) with one fp32 scale per 32 positions of a head
+// ([B, h, ceil(T / 32)]); o bf16, lse fp32 (may be null).
+struct PrefillFp8Args {
+    const void *q, *k, *v;
+    const float *q_scales, *k_scales, *v_scales;
+    void *o;
+    float *lse;
+    int B, T, hq, hkv;
+    int causal, window;
+    float scale;
+    const float *sinks;
+};
+hipError_t launch_prefill_fp8_d128(const PrefillFp8Args &a, hipStream_t stream);
+
 struct PrefillBwdArgs {
     const void *q, *k, *v, *o, *dout;
     const float *lse;
