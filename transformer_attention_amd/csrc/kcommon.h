@@ -143,17 +143,6 @@ __device__ __forceinline__ float finish_row_with_sink(float m, float l, float s2
     return z > 0.f ? f / z : 0.f;
 }
 
-// acc + the sum of the eight bf16 values of v (v_dot2_f32_bf16 against (1, 1):
-// two values per instruction; bf16 values times 1 are exact).
-__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
-    return acc;
-}
-
 // Value of lane (l ^ mask), through ds_bpermute (any mask < 64).
 __device__ __forceinline__ float shfl_xor(float x, int mask) {
     int lane = __lane_id();

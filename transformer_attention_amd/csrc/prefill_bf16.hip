@@ -81,6 +81,12 @@ constexpr float THR = 65536.0f;
 #ifndef PREFILL_NSTAGE
 #define PREFILL_NSTAGE 4
 #endif
+#ifndef PREFILL_KPF
+#define PREFILL_KPF 2       // k-steps of K operands read ahead of their MFMAs
+#endif
+#ifndef PREFILL_VPF
+#define PREFILL_VPF 3       // V operands read ahead of their MFMAs
+#endif
 
 struct Params {
     const __bf16 *q, *k, *v;
@@ -316,15 +322,16 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
     };
     // Probabilities of scores 8h .. 8h+7 of a key block against the reference
     // max m_use -> one bf16x8 B operand (keys 8(h/2)+4hi.. of the two row
-    // groups of that half); adds them to lsum.  The row sum adds the
-    // bf16-rounded probabilities (two per v_dot2 with (1, 1)): the same
-    // weights the P.V product uses.
+    // groups of that half); adds them to lsum.  The row sum adds the fp32
+    // probabilities with plain adds: v_dot2 (which could add the bf16 ones
+    // two at a time) waits for the matrix pipe, and with the other wave of
+    // the SIMD issuing MFMAs it takes about four times as long.
     auto probs8 = [&](const f32x16 &s, int h, float m_use, float &lsum, bf16x8 &pp) {
         float pv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(__builtin_fmaf(s[8 * h + i], c, -m_use));
         pp = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-        lsum = sum_bf16x8(pp, lsum);
+        lsum += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     };
     // Exponents are taken against 0 while a row has seen no visible key.
     auto m_ref = [](float m) { return m == -INFINITY ? 0.f : m; };
@@ -369,7 +376,11 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i)
         if (t_begin + i < t_end) issue_tile(t_begin + i);
-    wait_tiles(min(AHEAD - 1, t_end - t_begin - 1));  // tile tb landed (q loads are older)
+    // Wait for every load, Q and the prologue tiles alike (they were issued
+    // together): the compiler then knows the Q registers are complete and
+    // puts no wait for them inside the loop, where the only outstanding
+    // loads are the ring's copies, which it does not track.
+    wait_vmcnt<0>();
     raw_barrier();
 
     f32x16 sa[NB][KB], sb[NB][KB];
@@ -444,7 +455,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
                 pop[nb][0][1] = pc[nb][1];
             }
             // K operands are loaded KPF k-steps ahead of their MFMAs
-            constexpr int KPF = 2;
+            constexpr int KPF = PREFILL_KPF;
             bf16x8 ka[KPF + 1][KB];
 #pragma unroll
             for (int i = 0; i < KPF; ++i)
@@ -491,7 +502,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
             // P.V of tile t; key block 0 of tile t+1 is exponentiated under it
             // V operands are loaded VPF MFMA steps ahead
             constexpr int NV = KB * 2 * 4;            // (kb, half, db) steps
-            constexpr int VPF = 3;
+            constexpr int VPF = PREFILL_VPF;
             bf16x8 va[VPF + 1];
             auto vop = [&](int j) { return v_operand(vc, j & 3, j >> 3, (j >> 2) & 1); };
 #pragma unroll

@@ -369,6 +369,11 @@ void bwd_dkdv_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < KA_NSTAGE - 1; ++i)
         if (i < n_steps) issue_step(i);
+    // Every load so far (the wave's resident operands and the prologue
+    // copies) has landed: the compiler then puts no wait for the resident
+    // operands inside the loop, whose only outstanding loads are the ring's
+    // copies (which it does not track).
+    wait_vmcnt<0>();
 
     int cs_h = 0, cs_qt = qt_end - 1;           // step being computed
     for (int s = 0; s < n_steps; ++s) {
@@ -511,6 +516,11 @@ __global__ __launch_bounds__(64 * KB_WAVES, 1) void bwd_dq_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < KB_NSTAGE - 1; ++i)
         if (i < n_tiles) issue_tile(t_begin + i);
+    // Every load so far (the wave's resident operands and the prologue
+    // copies) has landed: the compiler then puts no wait for the resident
+    // operands inside the loop, whose only outstanding loads are the ring's
+    // copies (which it does not track).
+    wait_vmcnt<0>();
 
     for (int t = t_begin; t < t_end; ++t) {
         const int rel = t - t_begin;

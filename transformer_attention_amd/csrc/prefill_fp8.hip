@@ -230,6 +230,11 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
 #pragma unroll
     for (int i = 0; i < NSTAGE - 1; ++i)
         if (t_begin + i < t_end) issue_tile(t_begin + i);
+    // Every load so far (the wave's resident operands and the prologue
+    // copies) has landed: the compiler then puts no wait for the resident
+    // operands inside the loop, whose only outstanding loads are the ring's
+    // copies (which it does not track).
+    wait_vmcnt<0>();
 
     for (int t = t_begin; t < t_end; ++t) {
         const int rel = t - t_begin;
