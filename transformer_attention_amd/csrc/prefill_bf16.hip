@@ -281,21 +281,24 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
     };
     // Mask tile t in place (raw scores -> -inf where the key is not visible).
     // Element (kb, i) is key ts + 4hi + e with e = 32kb + 8(i/4) + (i%4).
+    // The visible keys of a row form one range of e, [lo, lo + width): below
+    // T, at or before the row (causal), within the window; one unsigned
+    // compare per element tests it.
     auto apply_mask = [&](int t, f32x16 (&s)[NB][KB]) {
         const int base = t * BN + 4 * hi;
-        const int lim_t = T - base;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int diff = row0 + 32 * nb - base;
+            int e_hi = min(T - base, BN);
+            if (p.causal) e_hi = min(e_hi, diff + 1);
+            const int lo = p.window > 0 ? min(max(diff - p.window + 1, 0), BN) : 0;
+            const uint32_t width = (uint32_t)max(e_hi - lo, 0);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int e = 32 * kb + 8 * (i >> 2) + (i & 3);
-                    bool vis = e < lim_t;
-                    if (p.causal) vis = vis && e <= diff;
-                    if (p.window > 0) vis = vis && diff - e < p.window;
-                    s[nb][kb][i] = vis ? s[nb][kb][i] : -INFINITY;
+                    s[nb][kb][i] = (uint32_t)(e - lo) < width ? s[nb][kb][i] : -INFINITY;
                 }
         }
     };
