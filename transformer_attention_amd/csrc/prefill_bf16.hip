@@ -125,27 +125,59 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
     const int q16 = lane >> 4;      // 16-lane group (for the transposing reads)
     const int j16 = lane & 15;
 
-    const int id = blockIdx.x;
-    const int rb = p.n_row_blocks - 1 - id / p.n_head_groups;
-    const int hg = id % p.n_head_groups;
-    const int subs = p.G / p.hpw;
-    const int sub = hg % subs;
-    const int g = (hg / subs) % p.hkv;
-    const int b = hg / (subs * p.hkv);
-    const int wph = NW / p.hpw;                       // waves per head (hpw <= NW)
-    const int h = g * p.G + sub * p.hpw + wave / wph;
-    const int r0 = rb * p.rows_per_wg;
-    const int rw0 = r0 + (wave % wph) * RW;
     const int T = p.T;
+    const int subs = p.G / p.hpw;
+    const int wph = NW / p.hpw;                       // waves per head (hpw <= NW)
 
-    // Key range of the workgroup and of this wave.
-    const int kend = p.causal ? min(T, r0 + p.rows_per_wg) : T;
-    const int kbeg = p.window > 0 ? max(0, r0 - p.window + 1) : 0;
-    const int t_begin = kbeg / BN;
-    const int t_end = (kend + BN - 1) / BN;
-    const bool wave_active = rw0 < T;
-    const int kend_w = p.causal ? min(T, rw0 + RW) : T;
-    const int kbeg_w = p.window > 0 ? max(0, rw0 - p.window + 1) : 0;
+    // Work items: (row block, head group) pairs numbered heaviest row block
+    // first with the head group fastest.  The grid is persistent: workgroup
+    // w takes items w, w + grid, ... of rounds 0, 1, ...; odd rounds run the
+    // round's items in reverse order within each residue class mod 8, so
+    // every workgroup's total (causal) work is about the same and all items
+    // of a workgroup keep its residue class of head groups (with 8 head
+    // groups: one K/V head, on the workgroup's XCD and its L2).
+    const int n_items = p.n_row_blocks * p.n_head_groups;
+    const int grid = gridDim.x;
+    auto item_id = [&](int k) {
+        int id = k * grid + blockIdx.x;
+        if ((k & 1) && grid % 8 == 0) id = k * grid + grid - 8 - 8 * (blockIdx.x / 8) + blockIdx.x % 8;
+        return id < n_items ? id : -1;
+    };
+    // Key tile range of item id and the offset of its K/V head.
+    auto item_tiles = [&](int id, int &tb, int &te, size_t &kvb) {
+        const int rb = p.n_row_blocks - 1 - id / p.n_head_groups;
+        const int hg = id % p.n_head_groups;
+        const int g = (hg / subs) % p.hkv;
+        const int b = hg / (subs * p.hkv);
+        const int r0 = rb * p.rows_per_wg;
+        const int kend = p.causal ? min(T, r0 + p.rows_per_wg) : T;
+        const int kbeg = p.window > 0 ? max(0, r0 - p.window + 1) : 0;
+        tb = kbeg / BN;
+        te = (kend + BN - 1) / BN;
+        kvb = ((size_t)b * p.hkv + g) * (size_t)T * D;
+    };
+
+    // The current item, as seen by this wave.
+    int b = 0, h = 0, rw0 = 0, t_begin = 0, t_end = 0, kend_w = 0, kbeg_w = 0;
+    bool wave_active = false;
+    size_t q_base = 0;
+    int row0 = 0;                                     // this lane's rows: row0 + 32 nb
+    auto set_item = [&](int id) {
+        const int rb = p.n_row_blocks - 1 - id / p.n_head_groups;
+        const int hg = id % p.n_head_groups;
+        const int sub = hg % subs;
+        const int g = (hg / subs) % p.hkv;
+        b = hg / (subs * p.hkv);
+        h = g * p.G + sub * p.hpw + wave / wph;
+        rw0 = rb * p.rows_per_wg + (wave % wph) * RW;
+        size_t kvb;
+        item_tiles(id, t_begin, t_end, kvb);
+        wave_active = rw0 < T;
+        kend_w = p.causal ? min(T, rw0 + RW) : T;
+        kbeg_w = p.window > 0 ? max(0, rw0 - p.window + 1) : 0;
+        q_base = ((size_t)b * p.hq + h) * (size_t)T * D;
+        row0 = rw0 + l32;
+    };
     auto tile_active = [&](int t) {
         const int ts = t * BN;
         return wave_active && t < t_end && ts < kend_w && ts + BN > kbeg_w;
@@ -156,44 +188,45 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
                (p.window > 0 && (rw0 + RW - 1) - ts >= p.window);
     };
 
-    const size_t kv_base = ((size_t)b * p.hkv + g) * (size_t)T * D;
-    const __bf16 *kg = p.k + kv_base;
-    const __bf16 *vg = p.v + kv_base;
-    const size_t q_base = ((size_t)b * p.hq + h) * (size_t)T * D;
-    const int row0 = rw0 + l32;                       // this lane's rows: row0 + 32 nb
     const float c = p.scale_log2;
 
     // Q^T B operands: row = row0 + 32nb, d = 16ks + 8hi .. +7
     bf16x8 qop[NB][8];
+    auto load_q = [&]() {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int row = row0 + 32 * nb;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (row < T) val = ldg16(p.q + q_base + (size_t)row * D + 16 * ks + 8 * hi);
-            qop[nb][ks] = __builtin_bit_cast(bf16x8, val);
-        }
+            for (int ks = 0; ks < 8; ++ks) {
+                const int row = row0 + 32 * nb;
+                u32x4 val = {0u, 0u, 0u, 0u};
+                if (row < T) val = ldg16(p.q + q_base + (size_t)row * D + 16 * ks + 8 * hi);
+                qop[nb][ks] = __builtin_bit_cast(bf16x8, val);
+            }
+    };
 
     f32x16 oacc[NB][4];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[nb][db][i] = 0.f;
     float m_run[NB], l_run[NB];
+    auto reset_rows = [&]() {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        m_run[nb] = -INFINITY;                        // reference max (log2 units)
-        l_run[nb] = 0.f;                              // lane-partial row sum
-    }
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[nb][db][i] = 0.f;
+            m_run[nb] = -INFINITY;                    // reference max (log2 units)
+            l_run[nb] = 0.f;                          // lane-partial row sum
+        }
+    };
 
     // LDS ring of NSTAGE stages, each holding the K and V rows of one tile.
-    // Tile t lives in stage (t - t_begin) % NSTAGE; at iteration t the stages
-    // hold tile t (V in use), t+1 (K in use), t+2 and t+3 (in flight).
-    auto kbuf = [&](int rel) { return smem + (rel % NSTAGE) * STAGE_BYTES; };
-    auto vbuf = [&](int rel) { return smem + (rel % NSTAGE) * STAGE_BYTES + KTILE_BYTES; };
+    // Tiles take the stages in the order they are copied, across items: the
+    // current item's first tile is number seq_f, its tile t lives in stage
+    // (seq_f + t - t_begin) % NSTAGE; at iteration t the stages hold tile t
+    // (V in use), t+1 (K in use) and the next two tiles of the sequence (in
+    // flight), which near an item's end are the next item's first tiles.
+    int seq_f = 0;
+    auto kbuf = [&](int rel) { return smem + ((seq_f + rel) % NSTAGE) * STAGE_BYTES; };
+    auto vbuf = [&](int rel) { return smem + ((seq_f + rel) % NSTAGE) * STAGE_BYTES + KTILE_BYTES; };
     // DMA of one tile: one-KB blocks (K rows, then V rows), split over the waves.
     // LDS byte o of a region holds row o / stride, chunk (o % stride) / 16;
     // pad slots receive an arbitrary valid chunk; rows past T re-read row T-1
@@ -222,11 +255,17 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
         dma_off[i] = (uint32_t)(r * D * 2 + ch * 16);
     }
     const uint32_t smem_lds = lds_offset(smem);
-    auto issue_tile = [&](int t) {
-        const uint32_t stage = smem_lds + ((t - t_begin) % NSTAGE) * STAGE_BYTES;
-        const int ts = t * BN;
-        const __bf16 *kb0 = kg + (size_t)ts * D;
-        const __bf16 *vb0 = vg + (size_t)ts * D;
+    // The copy stream: the next tile to copy is tile dma_t of item dma_id
+    // (-1 once every item's tiles are issued), sequence number dma_seq.
+    int dma_k = 0, dma_id = item_id(0), dma_t = 0, dma_te = 0, dma_seq = 0;
+    size_t dma_kv = 0;
+    if (dma_id >= 0) item_tiles(dma_id, dma_t, dma_te, dma_kv);
+    auto issue_next = [&]() {
+        if (dma_id < 0) return;
+        const uint32_t stage = smem_lds + (dma_seq % NSTAGE) * STAGE_BYTES;
+        const int ts = dma_t * BN;
+        const __bf16 *kb0 = p.k + dma_kv + (size_t)ts * D;
+        const __bf16 *vb0 = p.v + dma_kv + (size_t)ts * D;
         if (ts + BN <= T) {
 #pragma unroll
             for (int i = 0; i < PER_WAVE; ++i)
@@ -240,6 +279,11 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
                     ? dma_off[i] - (uint32_t)((dma_row[i] - last) * D * 2) : dma_off[i];
                 dma16_off_at(dma_is_v[i] ? vb0 : kb0, off, stage + min(PER_WAVE * wave + i, NBLK - 1) * 1024);
             }
+        }
+        ++dma_seq;
+        if (++dma_t == dma_te) {
+            dma_id = item_id(++dma_k);
+            if (dma_id >= 0) item_tiles(dma_id, dma_t, dma_te, dma_kv);
         }
     };
     static_assert(AHEAD <= 4, "wait counts below assume at most 4 tiles in flight");
@@ -375,24 +419,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
         }
     };
 
-    // ---- prologue: tiles tb .. tb+AHEAD-1 in flight; S(tb) and its max ----
-#pragma unroll
-    for (int i = 0; i < AHEAD; ++i)
-        if (t_begin + i < t_end) issue_tile(t_begin + i);
-    // Wait for every load, Q and the prologue tiles alike (they were issued
-    // together): the compiler then knows the Q registers are complete and
-    // puts no wait for them inside the loop, where the only outstanding
-    // loads are the ring's copies, which it does not track.
-    wait_vmcnt<0>();
-    raw_barrier();
-
     f32x16 sa[NB][KB], sb[NB][KB];
-    if (tile_active(t_begin)) {
-        qk(kbuf(0), sa);
-        if (tile_needs_mask(t_begin)) apply_mask(t_begin, sa);
-        start_rows(sa);
-        probs_block0(sa);
-    }
 
     // Some row of tile t overflowed the threshold: recompute the tile's scores from the K rows still in its stage
     // (bit for bit the same scores), move those rows' reference max to their
@@ -431,11 +458,11 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
     // tile t+1 into s_nxt.
     auto iteration = [&](int t, f32x16 (&s_cur)[NB][KB], f32x16 (&s_nxt)[NB][KB]) {
         const int rel = t - t_begin;
-        wait_tiles(min(AHEAD - 2, t_end - t - 2));    // tile t+1 landed
+        wait_tiles(min(AHEAD - 2, dma_seq - (seq_f + rel) - 2));   // tile t+1 landed
         raw_barrier();                                // iteration t-1 done everywhere
-        // the copy of tile t+AHEAD (into the stage of tile t-1) is issued
-        // between the first score MFMAs when this wave has a tile to compute
-        const bool dma_now = t + AHEAD < t_end;
+        // the copy of the tile AHEAD places on in the sequence (into the stage
+        // of tile t-1) is issued between the first score MFMAs when this wave
+        // has a tile to compute
 
         const bool act_c = tile_active(t);
         const bool act_n = tile_active(t + 1);
@@ -477,7 +504,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) smfma(ks, kb, nb, ka[ks % (KPF + 1)][kb], s_nxt[nb][kb]);
-                if (ks == 1 && dma_now) issue_tile(t + AHEAD);
+                if (ks == 1) issue_next();
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     if (ks == 1) { probs8(s_cur[nb][1], 0, m_use[nb], lsum[nb], pop[nb][1][0]); pin(pop[nb][1][0]); }
@@ -527,7 +554,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
-            if (dma_now) issue_tile(t + AHEAD);
+            issue_next();
             if (act_n) {                              // first tile of this wave
                 qk(kn, s_nxt);
                 if (tile_needs_mask(t + 1)) apply_mask(t + 1, s_nxt);
@@ -537,14 +564,9 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
         }
     };
 
-    int t = t_begin;
-    for (; t + 1 < t_end; t += 2) {
-        iteration(t, sa, sb);
-        iteration(t + 1, sb, sa);
-    }
-    if (t < t_end) iteration(t, sa, sb);
-
-    if (!wave_active) return;
+    char *epi_buf = smem;
+    static_assert(NB != 1 || 8 * 32 * 144 <= STAGE_BYTES, "epilogue staging exceeds a stage");
+    auto epilogue = [&]() {
     if constexpr (ASM_S) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -556,24 +578,92 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void prefill_bf16_d128_kernel(Par
     for (int nb = 0; nb < NB; ++nb) {
         const int row = row0 + 32 * nb;
         const float lt = pair32_sum(l_run[nb]);
-        if (row >= T) continue;
+        if (NB != 1 && row >= T) continue;
         float inv = lt > 0.f ? 1.0f / lt : 0.f;
         float lse_sink = 0.f;
         if (p.sinks) inv = finish_row_with_sink(m_run[nb], lt, p.sinks[h] * kLog2e, lse_sink);
-        __bf16 *orow = p.o + q_base + (size_t)row * D;
+        if constexpr (NB == 1) {
+            // Through LDS, so that the stores are whole 128-byte row halves:
+            // each lane holds four-value pieces of its row, which scattered
+            // 8-byte stores write one 16-byte piece per row at a time.  The
+            // wave's 32 rows x 64 values of one half go to its own region of
+            // the item's last stage (rows 144 bytes apart: the 8-byte writes of
+            // a quarter wave hit distinct banks), then come back as 16 bytes
+            // of 8 consecutive values per lane, 8 lanes per row half.
+            char *reg = epi_buf + wave * (32 * 144);
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+            for (int half = 0; half < 2; ++half) {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * db + 8 * q4 + 4 * hi;
-                u32x2 w = {pack_bf16x2(oacc[nb][db][4 * q4 + 0] * inv, oacc[nb][db][4 * q4 + 1] * inv),
-                           pack_bf16x2(oacc[nb][db][4 * q4 + 2] * inv, oacc[nb][db][4 * q4 + 3] * inv)};
-                *reinterpret_cast<u32x2 *>(orow + d) = w;
+                for (int db = 2 * half; db < 2 * half + 2; ++db)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int d = 32 * db + 8 * q4 + 4 * hi - 64 * half;
+                        u32x2 w = {pack_bf16x2(oacc[nb][db][4 * q4 + 0] * inv, oacc[nb][db][4 * q4 + 1] * inv),
+                                   pack_bf16x2(oacc[nb][db][4 * q4 + 2] * inv, oacc[nb][db][4 * q4 + 3] * inv)};
+                        *reinterpret_cast<u32x2 *>(reg + l32 * 144 + 2 * d) = w;
+                    }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int rr = 8 * r + (lane >> 3), ch = lane & 7;
+                    const u32x4 v4 = *reinterpret_cast<const u32x4 *>(reg + rr * 144 + 16 * ch);
+                    if (rw0 + rr < T)
+                        *reinterpret_cast<u32x4 *>(p.o + q_base + (size_t)(rw0 + rr) * D + 64 * half + 8 * ch) = v4;
+                }
             }
-        if (p.lse && hi == 0) {
+        } else {
+            __bf16 *orow = p.o + q_base + (size_t)row * D;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d = 32 * db + 8 * q4 + 4 * hi;
+                    u32x2 w = {pack_bf16x2(oacc[nb][db][4 * q4 + 0] * inv, oacc[nb][db][4 * q4 + 1] * inv),
+                               pack_bf16x2(oacc[nb][db][4 * q4 + 2] * inv, oacc[nb][db][4 * q4 + 3] * inv)};
+                    *reinterpret_cast<u32x2 *>(orow + d) = w;
+                }
+        }
+        if (p.lse && hi == 0 && row < T) {
             const size_t li = ((size_t)b * p.hq + h) * (size_t)T + row;
             p.lse[li] = p.sinks ? lse_sink : (lt > 0.f ? m_run[nb] * kLn2 + __logf(lt) : -INFINITY);
         }
+    }
+    };
+
+    // ---- the workgroup's items ----
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) issue_next();
+    for (int k = 0;; ++k) {
+        const int id = item_id(k);
+        if (id < 0) break;
+        set_item(id);
+        load_q();
+        reset_rows();
+        rows_started = false;
+        // Wait for every load, Q and the copies in flight alike: the compiler
+        // then knows the Q registers are complete and puts no wait for them
+        // inside the loop, where the only outstanding loads are the ring's
+        // copies, which it does not track.  (An item's first tiles were
+        // copied during the previous item's last tiles.)
+        wait_vmcnt<0>();
+        raw_barrier();
+        if (tile_active(t_begin)) {
+            qk(kbuf(0), sa);
+            if (tile_needs_mask(t_begin)) apply_mask(t_begin, sa);
+            start_rows(sa);
+            probs_block0(sa);
+        }
+        int t = t_begin;
+        for (; t + 1 < t_end; t += 2) {
+            iteration(t, sa, sb);
+            iteration(t + 1, sb, sa);
+        }
+        if (t < t_end) iteration(t, sa, sb);
+        // every wave is done with the item's last stage, which no copy in
+        // flight targets: the epilogue stages its output there
+        raw_barrier();
+        epi_buf = smem + ((seq_f + t_end - t_begin - 1) % NSTAGE) * STAGE_BYTES;
+        if (wave_active) epilogue();
+        seq_f += t_end - t_begin;
     }
 }
 
@@ -606,9 +696,15 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs &a, hipStream_t stream) {
     p.sinks = a.sinks;
     hipError_t e = ensure_dynamic_lds((const void *)prefill_bf16_d128_kernel<NB, KB, NST>, LDS_BYTES);
     if (e != hipSuccess) return e;
-    const long long nblocks = (long long)p.n_row_blocks * p.n_head_groups;
-    if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_bf16_d128_kernel<NB, KB, NST>), dim3((unsigned)nblocks), dim3(64 * NW),
+    const long long n_items = (long long)p.n_row_blocks * p.n_head_groups;
+    if (n_items <= 0) return hipSuccess;
+    // One persistent workgroup per compute unit (the LDS ring admits one).
+    int dev = 0, n_cu = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const long long grid = n_items < n_cu ? n_items : (long long)n_cu;
+    hipLaunchKernelGGL((prefill_bf16_d128_kernel<NB, KB, NST>), dim3((unsigned)grid), dim3(64 * NW),
                        LDS_BYTES, stream, p);
     return hipGetLastError();
 }
