@@ -222,7 +222,9 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
  *
  * score_j = scale * (q[:d_c] . c_j + q[d_c:] . kR_j); the value of token j
  * is the first d_c entries of the same cache row.  split_tokens and sinks
- * as for attn_decode.  Supported: d_c = 512, d_r = 64, h_q a multiple of 16.
+ * as for attn_decode; each chunk's normalised partial output is kept in
+ * bf16 in the workspace (mla_decode_workspace_size bytes) before the merge.
+ * Supported: d_c = 512, d_r = 64, h_q a multiple of 16.
  */
 size_t mla_decode_workspace_size(int B, int S_max, int h_q, int d_c, int d_r,
                                  int split_tokens);

@@ -68,6 +68,11 @@ size_t split_ws_bytes(long long rows, long long n_split, long long dv) {
     return align_up((size_t)(rows * n_split * dv) * sizeof(float), 256) +
            align_up((size_t)(rows * n_split) * sizeof(float), 256);
 }
+// The MLA decodes keep their normalised partial outputs in bf16.
+size_t mla_ws_bytes(long long rows, long long n_split, long long dv) {
+    return align_up((size_t)(rows * n_split * dv) * sizeof(uint16_t), 256) +
+           align_up((size_t)(rows * n_split) * sizeof(float), 256);
+}
 
 // Compute units of the current device (cached per device id).
 int device_cu_count() {
@@ -339,7 +344,7 @@ size_t mla_decode_workspace_size(int B, int S_max, int h_q, int d_c, int d_r, in
     if (split_tokens < 0 || split_tokens % 64) return 0;
     const int split = split_tokens ? split_tokens : default_mla_split(B, S_max, h_q);
     const long long ns = (S_max + split - 1) / split;
-    return split_ws_bytes((long long)B * h_q, ns, d_c);
+    return mla_ws_bytes((long long)B * h_q, ns, d_c);
 }
 
 attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *lse,
@@ -356,9 +361,9 @@ attn_status_t mla_decode(const void *q, const void *kv_cache, void *o, float *ls
     const int ns = (S_max + split - 1) / split;
     const size_t need = mla_decode_workspace_size(B, S_max, h_q, d_c, d_r, split_tokens);
     if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-    float *ws_o = static_cast<float *>(workspace);
+    __bf16 *ws_o = static_cast<__bf16 *>(workspace);
     float *ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                              align_up((size_t)B * h_q * ns * d_c * sizeof(float), 256));
+                                              align_up((size_t)B * h_q * ns * d_c * sizeof(uint16_t), 256));
     mi355::MlaArgs a{q, kv_cache, o, lse, seq_lens, B, S_max, h_q, d_c, d_r, scale, split, ns,
                      ws_o, ws_lse, nullptr, 0, 0, 0, sinks};
     return mi355::launch_mla_decode_bf16(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -388,8 +393,8 @@ attn_status_t mla_decode_fp8(const void *q, const void *kv_codes, const float *k
     if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     char *w = static_cast<char *>(workspace);
     const size_t rows = (size_t)B * h_q;
-    float *ws_o = reinterpret_cast<float *>(w);
-    w += align_up(rows * ns * d_c * sizeof(float), 256);
+    __bf16 *ws_o = reinterpret_cast<__bf16 *>(w);
+    w += align_up(rows * ns * d_c * sizeof(uint16_t), 256);
     float *ws_lse = reinterpret_cast<float *>(w);
     w += align_up(rows * ns * sizeof(float), 256);
     void *ws_q8 = w;
@@ -424,9 +429,9 @@ attn_status_t mla_decode_paged(const void *q, const void *kv_pages, void *o, flo
     const int ns = (S_max + split - 1) / split;
     const size_t need = mla_decode_workspace_size(B, S_max, h_q, d_c, d_r, split_tokens);
     if (bad_ptr(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-    float *ws_o = static_cast<float *>(workspace);
+    __bf16 *ws_o = static_cast<__bf16 *>(workspace);
     float *ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                              align_up((size_t)B * h_q * ns * d_c * sizeof(float), 256));
+                                              align_up((size_t)B * h_q * ns * d_c * sizeof(uint16_t), 256));
     mi355::MlaArgs a{q, kv_pages, o, lse, seq_lens, B, S_max, h_q, d_c, d_r, scale, split, ns,
                      ws_o, ws_lse, block_table, max_blocks, page_size, num_pages, sinks};
     return mi355::launch_mla_decode_bf16(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

@@ -488,8 +488,8 @@ __global__ __launch_bounds__(64 * Layout<FP8>::nw, 1) void decode_bf16_d128_kern
 // An optional sink logit per head (sinks[h], natural-log units like the
 // scaled scores) adds one more term to the merged denominator and carries no
 // value: Z = sum_s 2^(L_s - M) + 2^(sink log2 e - M).
-template <int DV>
-__global__ __launch_bounds__(256) void split_combine_kernel(const float *ws_o, const float *ws_lse,
+template <int DV, bool PB16>
+__global__ __launch_bounds__(256) void split_combine_kernel(const void *ws_o_, const float *ws_lse,
                                                             const int32_t *seq_lens, __bf16 *o, float *lse,
                                                             int n_rows, int H, int S_max, int split,
                                                             int n_split_max, const float *sinks) {
@@ -503,7 +503,15 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float *ws_o, c
     len = len < 0 ? 0 : (len > S_max ? S_max : len);
     const int ns = (len + split - 1) / split;
     const float *lrow = ws_lse + (size_t)row * n_split_max;
-    const float *orow = ws_o + (size_t)row * n_split_max * DV + PER * lane;
+    // partial s of this row: PER values per lane, fp32 or (PB16) bf16
+    typedef __attribute__((ext_vector_type(PER))) __bf16 bvec;
+    const char *orow = static_cast<const char *>(ws_o_) +
+                       ((size_t)row * n_split_max * DV + PER * lane) * (PB16 ? 2 : 4);
+    auto part = [&](int sidx) -> fvec {
+        const char *ptr = orow + (size_t)sidx * DV * (PB16 ? 2 : 4);
+        if constexpr (PB16) return __builtin_convertvector(*reinterpret_cast<const bvec *>(ptr), fvec);
+        else return *reinterpret_cast<const fvec *>(ptr);
+    };
 
     float M = -INFINITY;
     for (int c0 = 0; c0 < ns; c0 += 64)
@@ -529,8 +537,7 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float *ws_o, c
             for (; s + 4 <= cn; s += 4) {
                 fvec v[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    v[u] = *reinterpret_cast<const fvec *>(orow + (size_t)(c0 + s + u) * DV);
+                for (int u = 0; u < 4; ++u) v[u] = part(c0 + s + u);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const float ws = readlane_f32(w, s + u);
@@ -539,7 +546,7 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float *ws_o, c
                 }
             }
             for (; s < cn; ++s) {
-                const fvec v = *reinterpret_cast<const fvec *>(orow + (size_t)(c0 + s) * DV);
+                const fvec v = part(c0 + s);
                 const float ws = readlane_f32(w, s);
                 Z += ws;
                 acc += ws * v;
@@ -630,24 +637,22 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs &a, hipStream_t stream) {
                                 a.split, a.n_split_max, a.sinks, stream);
 }
 
-hipError_t launch_split_combine(const float *ws_o, const float *ws_lse, const int32_t *seq_lens,
+hipError_t launch_split_combine(const void *ws_o, const float *ws_lse, const int32_t *seq_lens,
                                 void *o, float *lse, int B, int H, int dv, int S_max, int split,
-                                int n_split_max, const float *sinks, hipStream_t stream) {
+                                int n_split_max, const float *sinks, hipStream_t stream,
+                                bool partial_bf16) {
     const long long n_rows = (long long)B * H;
     if (n_rows > 0x7fffffffLL - 4) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((n_rows + 3) / 4));
     __bf16 *ob = static_cast<__bf16 *>(o);
-    switch (dv) {
-        case 128:
-            hipLaunchKernelGGL(split_combine_kernel<128>, grid, dim3(256), 0, stream, ws_o, ws_lse,
-                               seq_lens, ob, lse, (int)n_rows, H, S_max, split, n_split_max, sinks);
-            break;
-        case 512:
-            hipLaunchKernelGGL(split_combine_kernel<512>, grid, dim3(256), 0, stream, ws_o, ws_lse,
-                               seq_lens, ob, lse, (int)n_rows, H, S_max, split, n_split_max, sinks);
-            break;
-        default: return hipErrorInvalidValue;
-    }
+    if (dv == 128 && !partial_bf16)
+        hipLaunchKernelGGL((split_combine_kernel<128, false>), grid, dim3(256), 0, stream, ws_o, ws_lse,
+                           seq_lens, ob, lse, (int)n_rows, H, S_max, split, n_split_max, sinks);
+    else if (dv == 512 && partial_bf16)
+        hipLaunchKernelGGL((split_combine_kernel<512, true>), grid, dim3(256), 0, stream, ws_o, ws_lse,
+                           seq_lens, ob, lse, (int)n_rows, H, S_max, split, n_split_max, sinks);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

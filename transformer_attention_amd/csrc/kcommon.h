@@ -143,6 +143,39 @@ __device__ __forceinline__ float finish_row_with_sink(float m, float l, float s2
     return z > 0.f ? f / z : 0.f;
 }
 
+// One split's normalised partial outputs of the MLA decode, stored as bf16
+// rows through LDS.  The wave's 32 heads x 32*NDB values sit in O^T
+// accumulators (element i of d-block db is value 32db + 8(i/4) + 4hh + (i%4)
+// of head column l32); they go to the wave's own region of `lds` (rows
+// 2*DV + 16 bytes apart), then each store writes one head's whole row.
+// row0 is the partial-row index of the wave's first head, rows of
+// consecutive heads are n_split apart, and only the first n_valid heads
+// are stored.  The caller makes sure no wave still reads the region.
+template <int NDB>
+__device__ __forceinline__ void store_partial_rows(char *lds, int wave, int lane, const f32x16 (&oacc)[NDB],
+                                                   float inv, __bf16 *ws_o, size_t row0, int n_split,
+                                                   int n_valid) {
+    constexpr int DV = 32 * NDB;
+    constexpr int PITCH = 2 * DV + 16;
+    static_assert(2 * DV == 64 * 16, "one 16-byte piece per lane covers a row");
+    char *reg = lds + wave * 32 * PITCH;
+    const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                             pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+            *reinterpret_cast<u32x2 *>(reg + l32 * PITCH + 2 * (32 * db + 8 * g + 4 * hh)) = w;
+        }
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+        if (r >= n_valid) break;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(reg + r * PITCH + 16 * lane);
+        *reinterpret_cast<u32x4 *>(ws_o + (row0 + (size_t)r * n_split) * DV + 8 * lane) = v;
+    }
+}
+
 // Value of lane (l ^ mask), through ds_bpermute (any mask < 64).
 __device__ __forceinline__ float shfl_xor(float x, int mask) {
     int lane = __lane_id();

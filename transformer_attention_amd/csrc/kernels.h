@@ -95,7 +95,7 @@ struct MlaArgs {
     float scale;
     int split;
     int n_split_max;
-    float *ws_o;          // [B, H, n_split_max, d_c]
+    __bf16 *ws_o;         // [B, H, n_split_max, d_c] bf16 (normalised partial outputs)
     float *ws_lse;        // [B, H, n_split_max]  (log2 units)
     // paged cache (block_table == nullptr: contiguous [B, S_max, d_c + d_r]):
     // cache is [num_pages, page_size, d_c + d_r], S_max = max_blocks * page_size
@@ -118,7 +118,8 @@ struct MlaFp8Args {
     int B, S_max, H;
     float scale;
     int split, n_split_max;     // split: a multiple of 64
-    float *ws_o, *ws_lse;       // as MlaArgs
+    __bf16 *ws_o;               // as MlaArgs
+    float *ws_lse;
     void *ws_q8;                // [B, H, d_c + d_r] query codes
     float *ws_qs;               // [B, H] query scales
     const float *sinks;
@@ -144,9 +145,11 @@ hipError_t launch_quantize_kv_fp8(const void *x, void *codes, float *scales, lon
 // Merge of split partials: o[b,h,:] (bf16) and lse[b,h] (natural log, may be
 // null) from ws_o/ws_lse over the ceil(len_b / split) splits of sequence b;
 // sinks (per head, may be null) adds a sink logit to each merged denominator.
-hipError_t launch_split_combine(const float *ws_o, const float *ws_lse,
+// ws_o holds fp32 partials (GQA decode) or, with partial_bf16, bf16 ones (MLA).
+hipError_t launch_split_combine(const void *ws_o, const float *ws_lse,
                                 const int32_t *seq_lens, void *o, float *lse,
                                 int B, int H, int dv, int S_max, int split,
-                                int n_split_max, const float *sinks, hipStream_t stream);
+                                int n_split_max, const float *sinks, hipStream_t stream,
+                                bool partial_bf16 = false);
 
 }  // namespace mi355

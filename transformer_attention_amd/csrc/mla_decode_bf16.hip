@@ -62,7 +62,8 @@ struct Params {
     // (entries clamped to [0, num_pages - 1])
     const int32_t *block_table;
     int max_blocks, page_size, num_pages;
-    float *ws_o, *ws_lse;
+    __bf16 *ws_o;
+    float *ws_lse;
     int B, S_max, H;
     int split, n_split_max, n_hchunk;
     float scale_log2;
@@ -308,20 +309,15 @@ void mla_decode_kernel(Params p) {
     }
 
     const float lt = pair32_sum(l_run);
-    if (!head_ok) return;
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const size_t ws = ((size_t)b * p.H + h) * p.n_split_max + s;
-    float *wo = p.ws_o + ws * DC;
-    // O^T element i of d-block db is d = 32db + 8(i/4) + 4hh + (i%4) of head column l32
-#pragma unroll
-    for (int db = 0; db < DC / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            f32x4 v = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                       oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
-            *reinterpret_cast<f32x4 *>(wo + 32 * db + 8 * g + 4 * hh) = v;
-        }
-    if (hh == 0) p.ws_lse[ws] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
+    // The normalised partial O goes out as bf16 through LDS, so that every
+    // store writes one head's whole 1-KB row (straight from the registers
+    // each store would touch 32 heads' rows, 32 bytes apiece).  All tiles
+    // have landed and every wave is past its last read of the ring.
+    raw_barrier();
+    store_partial_rows(smem, wave, lane, oacc, inv, p.ws_o, ((size_t)b * p.H + hc * HPC + wave * HPW) * p.n_split_max + s,
+                       p.n_split_max, p.H - (hc * HPC + wave * HPW));
+    if (head_ok && hh == 0) p.ws_lse[((size_t)b * p.H + h) * p.n_split_max + s] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
 }
 
 }  // namespace
@@ -358,7 +354,7 @@ hipError_t launch_mla_decode_bf16(const MlaArgs &a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_combine(a.ws_o, a.ws_lse, a.seq_lens, a.o, a.lse, a.B, a.H, DC, a.S_max,
-                                a.split, a.n_split_max, a.sinks, stream);
+                                a.split, a.n_split_max, a.sinks, stream, /*partial_bf16=*/true);
 }
 
 }  // namespace mi355

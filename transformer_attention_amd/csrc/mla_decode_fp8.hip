@@ -78,7 +78,8 @@ struct Params {
     const uint8_t *c;           // [B, S_max, DK] cache codes
     const float *cs;            // [B, n_stiles] cache scales
     const int32_t *seq_lens;
-    float *ws_o, *ws_lse;
+    __bf16 *ws_o;
+    float *ws_lse;
     int B, S_max, H, n_stiles;
     int split, n_split_max, n_hchunk;
     float scale_log2;           // scale * log2(e)
@@ -352,19 +353,13 @@ void mla_decode_fp8_kernel(Params p) {
     for (int db = 0; db < DC / 32; ++db) settle_acc(oacc[db]);
 
     const float lt = pair32_sum(l_run);
-    if (!head_ok) return;
     const float inv = lt > 0.f ? 1.0f / (448.0f * lt) : 0.f;
-    const size_t ws = ((size_t)b * p.H + h) * p.n_split_max + s;
-    float *wo = p.ws_o + ws * DC;
-#pragma unroll
-    for (int db = 0; db < DC / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            f32x4 v = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                       oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
-            *reinterpret_cast<f32x4 *>(wo + 32 * db + 8 * g + 4 * hh) = v;
-        }
-    if (hh == 0) p.ws_lse[ws] = lt > 0.f ? R + __log2f(lt) : -INFINITY;
+    // bf16 partial rows through LDS, one whole row per store (see the bf16
+    // kernel); all tiles have landed and every wave is past the ring.
+    raw_barrier();
+    store_partial_rows(smem, wave, lane, oacc, inv, p.ws_o, ((size_t)b * p.H + hc * HPC + wave * HPW) * p.n_split_max + s,
+                       p.n_split_max, p.H - (hc * HPC + wave * HPW));
+    if (head_ok && hh == 0) p.ws_lse[((size_t)b * p.H + h) * p.n_split_max + s] = lt > 0.f ? R + __log2f(lt) : -INFINITY;
 }
 
 }  // namespace
@@ -397,7 +392,7 @@ hipError_t launch_mla_decode_fp8(const MlaFp8Args &a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_combine(a.ws_o, a.ws_lse, a.seq_lens, a.o, a.lse, a.B, a.H, DC, a.S_max,
-                                a.split, a.n_split_max, a.sinks, stream);
+                                a.split, a.n_split_max, a.sinks, stream, /*partial_bf16=*/true);
 }
 
 }  // namespace mi355
