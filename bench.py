@@ -45,7 +45,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 # rocprofv3 FETCH_SIZE/WRITE_SIZE summaries (KiB per dispatch), scaled by the
 # same counters read on a plain copy kernel of known size; None until taken
 # for the current kernel.
-PREFILL_TRAFFIC_BYTES = 212685895   # prefill_bf16_d128 kernel <1,2,4>: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB
+PREFILL_TRAFFIC_BYTES = 211314853   # prefill_bf16_d128 kernel <1,2,4>: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB
 
 
 def prefill_visible_pairs(T: int, causal: bool, window: int) -> int:
@@ -66,10 +66,28 @@ def prefill_flops(shape) -> int:
 LAST_MEDIAN_MS = {}
 
 
+SPIN_UP_S = 0.25
+
+
+def _spin_up(torch, fn):
+    """Keeps the GPU busy with `fn` for SPIN_UP_S seconds, untimed, so that the
+    timed calls run at the device's steady clocks: from idle the MI355X takes
+    far longer than a few calls to raise them (five warm-up calls of the
+    Llama-3-8B prefill measured 0.596 ms per call, against 0.521 ms after
+    200 warm-up calls, on the same box)."""
+    t_end = time.perf_counter() + SPIN_UP_S
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def _events_time(torch, fn, steps, warmup, stream, key=None):
     """Mean milliseconds per call over `steps` back-to-back calls (HIP events
-    on `stream` around each call), after `warmup` untimed calls; the median
-    of the per-call durations is kept in LAST_MEDIAN_MS[key]."""
+    on `stream` around each call), after the spin-up and `warmup` untimed
+    calls; the median of the per-call durations is kept in
+    LAST_MEDIAN_MS[key]."""
+    _spin_up(torch, fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -451,8 +469,10 @@ def main(argv=None):
         "n_gpus": 1, "steps": steps, "warmup": warmup,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic N(0,1), seeded",
-        "timing": "HIP events on the library's stream around each call; ms = mean of the timed "
-                  "calls, median_ms = their median",
+        "timing": f"HIP events on the library's stream around each call; ms = mean of the timed "
+                  f"calls, median_ms = their median; each workload first keeps the GPU busy with the "
+                  f"same call for {SPIN_UP_S} s (untimed, so that the clocks are at their steady "
+                  f"state), then runs the warm-up calls, then the timed ones",
         "library": _library_info(ta),
     }
     first = selected[0]
