@@ -262,9 +262,19 @@ void bwd_dkdv_kernel(Params p) {
     // (asm MFMAs that carry their own wait states: mfma_s_first /
     // mfma_s_last / mfma_o_acc), so the compiler never moves the output
     // accumulators through VGPRs.
-    auto step_rows = [&](auto masked, const char *qtile, const char *gtile, const char *stat,
+    // The rows of a tile that see this lane's key form one range of the row
+    // offset e within the tile: at or after the key (causal), before T, less
+    // than the window past the key; [m_lo, m_lo + m_width) when need_mask.
+    auto step_rows = [&](bool need_mask, const char *qtile, const char *gtile, const char *stat,
                          int r0) {
-        constexpr bool MASKED = decltype(masked)::value;
+        int m_lo = 0;
+        uint32_t m_width = 0;
+        if (need_mask) {
+            int e_hi = T - r0;
+            if (p.window > 0) e_hi = min(e_hi, key + p.window - r0);
+            m_lo = p.causal ? max(key - r0, 0) : 0;
+            m_width = (uint32_t)max(min(e_hi, TROWS) - m_lo, 0);
+        }
         // (not unrolled: one block at a time keeps the live registers of a
         // single block)
 #pragma unroll 1
@@ -318,18 +328,17 @@ void bwd_dkdv_kernel(Params p) {
             for (int i = 0; i < 16; ++i) {
                 const float l2e = st[i >> 1][2 * (i & 1)];
                 const float dde = st[i >> 1][2 * (i & 1) + 1];
-                float pe = fast_exp2(__builtin_fmaf(sacc[i], c, -l2e));
-                float de = pe * (pacc[i] - dde);
-                if constexpr (MASKED) {
-                    const int qi = r0 + 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    bool vis = qi < T;
-                    if (p.causal) vis = vis && key <= qi;
-                    if (p.window > 0) vis = vis && qi - key < p.window;
-                    pe = vis ? pe : 0.f;
-                    de = vis ? de : 0.f;
+                pv[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -l2e));
+                dsv[i] = pv[i] * (pacc[i] - dde);
+            }
+            if (need_mask) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int e = 32 * mb + 8 * (i >> 2) + 4 * hi + (i & 3);
+                    const bool vis = (uint32_t)(e - m_lo) < m_width;
+                    pv[i] = vis ? pv[i] : 0.f;
+                    dsv[i] = vis ? dsv[i] : 0.f;
                 }
-                pv[i] = pe;
-                dsv[i] = de;
             }
             bf16x8 pb[2], sb[2];
 #pragma unroll
@@ -393,8 +402,7 @@ void bwd_dkdv_kernel(Params p) {
         const char *qtile = smem + (s % KA_NSTAGE) * KA_STAGE;
         const char *gtile = qtile + TBYTES;
         const char *stat = gtile + TBYTES;
-        if (need_mask) step_rows(std::true_type{}, qtile, gtile, stat, r0);
-        else step_rows(std::false_type{}, qtile, gtile, stat, r0);
+        step_rows(need_mask, qtile, gtile, stat, r0);
     }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
