@@ -562,15 +562,20 @@ __global__ __launch_bounds__(64 * KB_WAVES, 1) void bwd_dq_kernel(Params p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float pe = fast_exp2(__builtin_fmaf(sacc[i], c, -l2row));
-                float de = pe * (pacc[i] - ddrow);
-                if (need_mask) {
-                    const int kj = ts + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    bool vis = kj < T;
-                    if (p.causal) vis = vis && kj <= row0;
-                    if (p.window > 0) vis = vis && row0 - kj < p.window;
-                    de = vis ? de : 0.f;
+                dsv[i] = pe * (pacc[i] - ddrow);
+            }
+            // the keys this row sees form one range of the offset e within
+            // the tile: below T, at or before the row, within the window
+            if (need_mask) {
+                int e_hi = min(T - ts, TROWS);
+                if (p.causal) e_hi = min(e_hi, row0 - ts + 1);
+                const int lo = p.window > 0 ? min(max(row0 - ts - p.window + 1, 0), TROWS) : 0;
+                const uint32_t width = (uint32_t)max(e_hi - lo, 0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int e = 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
+                    dsv[i] = (uint32_t)(e - lo) < width ? dsv[i] : 0.f;
                 }
-                dsv[i] = de;
             }
             bf16x8 sb[2];
 #pragma unroll
