@@ -114,7 +114,7 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
  * s_ij = scale * sq_i * sk_j * (q8_i . k8_j).  Each row's probabilities are
  * quantised to E4M3 in 64-key tiles against the row's reference R, with the
  * value scale of their key folded in: e = 448 * 2^(y - R), y = s log2(e) +
- * log2(sv_j); when a tile's max of y exceeds R, R moves to that max plus 3
+ * log2(sv_j); when a tile's max of y exceeds R, R moves to that max plus 5
  * (log2 units), so no weight passes 448.  o = sum_j e_j v8_j / (448 l), l =
  * sum_j 2^(s_ij log2(e) - R) unquantised; lse = (R + log2 l) ln 2.  causal,
  * window, scale and sinks as for attn_prefill; masked keys inside a visited
@@ -360,7 +360,7 @@ attn_status_t attn_decode_paged_fp8(const void *q, const void *k_pages, const vo
  * s_j = scale * sq * sc_j * (q8 . c8_j).  The probabilities are quantised to
  * E4M3 in 64-token tiles against each chunk's reference R, with the value
  * scale of their token folded in: e_j = 448 * 2^(y_j - R), y_j = s_j log2(e)
- * + log2(sc_j); when a tile's max of y exceeds R, R moves to that max plus 3
+ * + log2(sc_j); when a tile's max of y exceeds R, R moves to that max plus 5
  * (log2 units), so no weight passes 448.  The output is sum_j e_j c8_j /
  * (448 l) with the unquantised denominator l = sum_j 2^(s_j log2(e) - R).
  * Chunks (and the sink) merge by their log-sum-exp.  The result differs from

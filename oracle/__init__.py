@@ -330,7 +330,7 @@ def mla_decode_fp8(q, codes, scales, seq_lens, *, d_c: int, d_r: int, scale: flo
     [B, S_max, d_c+d_r] with one scale per 32 tokens [B, ceil(S_max/32)],
     both products on the dequantised codes, the probabilities quantised to
     E4M3 against each chunk's reference (chunks of ``split`` tokens, compute
-    tiles of ``tile`` tokens; the reference moves to a tile's max plus 3, in
+    tiles of ``tile`` tokens; the reference moves to a tile's max plus 5, in
     log2 units, when the tile exceeds it) with the value scale folded in, the
     denominator from the unquantised probabilities.  Returns (o:[B,H,d_c],
     lse:[B,H])."""
@@ -361,7 +361,7 @@ def prefill_fp8(q8, q_scales, k8, k_scales, v8, v_scales, *, causal: bool, windo
     [B,h,ceil(T/32)] (the cache quantiser's layout), both products on the
     dequantised codes, each row's probabilities quantised to E4M3 against
     its reference (keys in ``tile``-aligned tiles; the reference moves to a
-    tile's max plus 3, log2 units, when the tile exceeds it) with the value
+    tile's max plus 5, log2 units, when the tile exceeds it) with the value
     scale folded in, the denominator from the unquantised probabilities.
     ``rows`` optionally lists the query positions to evaluate.  Returns
     (o:[B,hq,n_rows,d], lse:[B,hq,n_rows])."""

@@ -612,8 +612,8 @@ int oracle_decode_fp8(const float *q, const unsigned char *k8, const unsigned ch
  *     taken in chunks of `split` tokens and each chunk in compute tiles of
  *     `tile` tokens in order.  The chunk keeps a reference R (-inf at the
  *     start); before a tile's weights are taken, if the tile's max of y
- *     exceeds R, R moves to that max plus MLA_FP8_HEADROOM (3, in log2
- *     units), so later tiles may rise by up to 2^3 before R has to move
+ *     exceeds R, R moves to that max plus MLA_FP8_HEADROOM (5, in log2
+ *     units), so later tiles may rise by up to 2^5 before R has to move
  *     again;
  *  5. p is quantised to E4M3 against that reference: P8_j = E4M3(min(448,
  *     448 * 2^(y_j - R))) with the value scale folded in -- the pages' p /
@@ -630,7 +630,7 @@ int oracle_decode_fp8(const float *q, const unsigned char *k8, const unsigned ch
  * ceil(S_max/32)] scales; o:[B,H,dc]; lse:[B,H].  split and tile are
  * positive multiples of 32, tile divides split.
  */
-#define MLA_FP8_HEADROOM 3.0
+#define MLA_FP8_HEADROOM 5.0
 
 int oracle_mla_decode_fp8(const float *q, const unsigned char *c8, const float *cs,
                           const int *seq_lens, double *o, double *lse,

@@ -16,11 +16,12 @@
 //  * The weight of token j in the value product carries its tile's scale:
 //    y_j = s_j log2(e) + log2(sc_j).  Each chunk keeps a reference R: before
 //    a 64-token compute tile's weights are taken, if the tile's max of y
-//    exceeds R, R moves to that max plus HEADROOM (3, log2 units) and the
-//    output accumulated so far is rescaled by 2^(R_old - R_new).  With 32
-//    heads per wave, moving R to every new max would rescale the 256
-//    accumulators of a wave on most tiles; with the headroom a head must
-//    rise 8x to move it again.  The weights are quantised as e = 448 *
+//    exceeds R, R moves to that max plus HEADROOM (5, log2 units) and the
+//    output accumulated so far is rescaled by 2^(R_old - R_new).  The
+//    rescale touches all 256 accumulators of a wave whenever any of its 32
+//    heads moves: moving R to every new max did that on most tiles, and with
+//    3 units of headroom still on about a third of them; with 5 a head must
+//    rise 32x to move it again.  The weights are quantised as e = 448 *
 //    2^(y - R) -> E4M3 (the page's p / (amax / 448) with amax bounded by
 //    2^R: no weight passes 448), and the product accumulates e * c8.
 //    Folding the value scale into the weight lets one 64-token FP8 product
@@ -68,7 +69,7 @@ constexpr int NW = 4;                     // waves per workgroup
 constexpr int HPW = 32;                   // heads per wave
 constexpr int HPC = NW * HPW;             // heads per workgroup
 constexpr float LOG2_448 = 8.807354922057604f;
-constexpr float HEADROOM = 3.0f;          // log2 units above a new max
+constexpr float HEADROOM = 5.0f;          // log2 units above a new max
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 

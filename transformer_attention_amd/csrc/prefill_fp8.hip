@@ -13,7 +13,7 @@
 //    tile, scaled once per 32-key block;
 //  * the weight of key j carries its value scale, y_ij = s_ij log2(e) +
 //    log2(sv_j), and is quantised as e = 448 * 2^(y - R) -> E4M3 against the
-//    row's reference R; R moves to a tile's max plus HEADROOM (3, log2
+//    row's reference R; R moves to a tile's max plus HEADROOM (5, log2
 //    units) when the tile exceeds it, and what was accumulated is rescaled
 //    by 2^(R_old - R_new), so no weight passes 448 and rescales are rare;
 //  * the numerator accumulates e * v8, the denominator the unquantised
@@ -55,7 +55,7 @@ constexpr int PER_WAVE = (NBLK + NW - 1) / NW; // 3 (the last wave repeats its f
 constexpr int NSTAGE = 4;
 constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;   // 86016
 constexpr float LOG2_448 = 8.807354922057604f;
-constexpr float HEADROOM = 3.0f;
+constexpr float HEADROOM = 5.0f;
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
