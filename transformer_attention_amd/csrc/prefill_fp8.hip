@@ -88,10 +88,13 @@ __device__ __forceinline__ f32x16 mfma8_last(i32x8 a, i32x8 b, f32x16 c) {
         : "+v"(c) : "v"(a), "v"(b));
     return c;
 }
-// the output product through the compiler (block-scaled form, both scale
-// exponents 127: x 1.0)
-__device__ __forceinline__ f32x16 mfma8_o(i32x8 a, i32x8 b, f32x16 acc) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+// The output product through the compiler (block-scaled form, both scale
+// exponents 127: x 1.0), its accumulators in VGPRs like everything else: an
+// accumulator pinned in AGPRs made the compiler split the 256 registers
+// 128 / 128 and spill the rest of the loop's values through AGPRs on every
+// tile.
+__device__ __forceinline__ void mfma8_o(i32x8 a, i32x8 b, f32x16 &acc) {
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
 }
 __device__ __forceinline__ i32x8 lds32(const char *p) {
     const u32x4 lo = *reinterpret_cast<const u32x4 *>(p);
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
                 const float f = fast_exp2(R - Rn);   // 0 while R = -inf
                 if (R != -INFINITY) {
 #pragma unroll
-                    for (int db = 0; db < 4; ++db) scale_acc(oacc[db], f);
+                    for (int db = 0; db < 4; ++db) oacc[db] *= f;
                 }
                 l_run *= f;
                 R = Rn;
@@ -330,14 +333,12 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
             if (db + 1 < 4) va[(db + 1) & 1] = v_at(db + 1);
-            oacc[db] = mfma8_o(va[db & 1], pop, oacc[db]);
+            mfma8_o(va[db & 1], pop, oacc[db]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 
     if (!wave_active) return;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) settle_acc(oacc[db]);
     const float lt = pair32_sum(l_run);
     if (row >= T) return;
     float inv = lt > 0.f ? 1.0f / (448.0f * lt) : 0.f;
