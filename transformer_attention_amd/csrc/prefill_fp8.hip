@@ -34,6 +34,10 @@
 //    transposed with ds_read_b64_tr_b8 (four reads whose rows are the keys
 //    the lane's weights belong to; the FP8 MFMA pairs byte b of lane-half h
 //    of A with byte b of lane-half h of B, measured on the hardware);
+//  * the tile's max of y is taken only when the weights, taken against the
+//    current R, sum past 448 in some lane (or a row has no R yet): positive
+//    weights with a sum of at most 448 are each at most 448, so R moves on
+//    the same tiles as with the max taken every time;
 //  * LDS rows: K at slot 8 r + r/2 (16-row score reads of a quarter wave hit
 //    16 distinct slots), V at slot 12 r + (r/4) mod 4 (the 8-row transposing
 //    reads of a half wave hit 16 distinct slots).
@@ -280,16 +284,37 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
         const float sv1 = two ? ld_uniform_f(vsg, st0 + 1) : sv0;
         const float A0 = a_row * sk0, A1 = a_row * sk1;
         const float lb0 = __log2f(sv0), lb1 = __log2f(sv1);
-        float mx0 = -INFINITY, mx1 = -INFINITY;
+        // The weights against the current reference.  They are positive, so
+        // a lane whose weights sum to at most 448 has none above 448, i.e. no
+        // y above R: only when some lane's sum passes 448 (or a row's R is
+        // still -inf) is the tile's max of y taken, R moved for the rows whose
+        // max exceeds it, and the weights taken again -- R moves on exactly
+        // the tiles it would with the max taken every time.
+        float wt[2][16];
+        float sum0, sum1;
+        auto take_weights = [&]() {
+            const float R_use = R == -INFINITY ? 0.f : R;
+            const float bb0 = lb0 + LOG2_448 - R_use, bb1 = lb1 + LOG2_448 - R_use;
+            sum0 = 0.f;
+            sum1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            mx0 = fmaxf(mx0, sacc[0][i]);
-            mx1 = fmaxf(mx1, sacc[1][i]);
-        }
-        const float ym = fmaxf(__builtin_fmaf(mx0, A0, lb0), __builtin_fmaf(mx1, A1, lb1));
-        if (__any(ym > R)) {                         // some row's reference moves
-            const float yh = pair32_max(ym);
-            if (yh > R) {
+            for (int i = 0; i < 16; ++i) {
+                wt[0][i] = fast_exp2(__builtin_fmaf(sacc[0][i], A0, bb0));
+                wt[1][i] = fast_exp2(__builtin_fmaf(sacc[1][i], A1, bb1));
+                sum0 += wt[0][i];
+                sum1 += wt[1][i];
+            }
+        };
+        take_weights();
+        if (__any(R == -INFINITY || !(sum0 + sum1 <= 448.0f))) {
+            float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                mx0 = fmaxf(mx0, sacc[0][i]);
+                mx1 = fmaxf(mx1, sacc[1][i]);
+            }
+            const float yh = pair32_max(fmaxf(__builtin_fmaf(mx0, A0, lb0), __builtin_fmaf(mx1, A1, lb1)));
+            if (yh > R) {                            // this row's reference moves
                 const float Rn = yh + HEADROOM;
                 const float f = fast_exp2(R - Rn);   // 0 while R = -inf
                 if (R != -INFINITY) {
@@ -299,23 +324,14 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
                 l_run *= f;
                 R = Rn;
             }
-        }
-        const float R_use = R == -INFINITY ? 0.f : R;
-        const float bb0 = lb0 + LOG2_448 - R_use, bb1 = lb1 + LOG2_448 - R_use;
-        float sum0 = 0.f, sum1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            sacc[0][i] = fast_exp2(__builtin_fmaf(sacc[0][i], A0, bb0));
-            sacc[1][i] = fast_exp2(__builtin_fmaf(sacc[1][i], A1, bb1));
-            sum0 += sacc[0][i];
-            sum1 += sacc[1][i];
+            take_weights();
         }
         l_run += sum0 * __builtin_amdgcn_rcpf(448.0f * sv0) + sum1 * __builtin_amdgcn_rcpf(448.0f * sv1);
         i32x8 pop;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            pop[k] = pack_fp8x4(sacc[0][4 * k], sacc[0][4 * k + 1], sacc[0][4 * k + 2], sacc[0][4 * k + 3]);
-            pop[4 + k] = pack_fp8x4(sacc[1][4 * k], sacc[1][4 * k + 1], sacc[1][4 * k + 2], sacc[1][4 * k + 3]);
+            pop[k] = pack_fp8x4(wt[0][4 * k], wt[0][4 * k + 1], wt[0][4 * k + 2], wt[0][4 * k + 3]);
+            pop[4 + k] = pack_fp8x4(wt[1][4 * k], wt[1][4 * k + 1], wt[1][4 * k + 2], wt[1][4 * k + 3]);
         }
         __builtin_amdgcn_sched_barrier(0);
 
