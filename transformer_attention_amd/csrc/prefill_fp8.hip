@@ -106,8 +106,11 @@ __device__ __forceinline__ i32x8 lds32(const char *p) {
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
-__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+// Four E4M3 codes in one word.  The first conversion writes the low half and
+// keeps the high half of `old`, which the second then overwrites: passing the
+// word's previous contents (rather than 0) spares a register clear per word.
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d, int old) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -187,12 +190,18 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
         const int ts = t * BN;
         const uint8_t *kb0 = kg + (size_t)ts * D;
         const uint8_t *vb0 = vg + (size_t)ts * D;
-        const int last = T - 1 - ts;
+        if (ts + BN <= T) {                          // whole tile: precomputed offsets
 #pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            const uint32_t off = dma_row[i] > last
-                ? dma_off[i] - (uint32_t)((dma_row[i] - last) * D) : dma_off[i];
-            dma16_off_at(dma_v[i] ? vb0 : kb0, off, stage + min(PER_WAVE * wave + i, NBLK - 1) * 1024);
+            for (int i = 0; i < PER_WAVE; ++i)
+                dma16_off_at(dma_v[i] ? vb0 : kb0, dma_off[i], stage + min(PER_WAVE * wave + i, NBLK - 1) * 1024);
+        } else {                                     // ragged last tile: rows past T re-read row T-1
+            const int last = T - 1 - ts;
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) {
+                const uint32_t off = dma_row[i] > last
+                    ? dma_off[i] - (uint32_t)((dma_row[i] - last) * D) : dma_off[i];
+                dma16_off_at(dma_v[i] ? vb0 : kb0, off, stage + min(PER_WAVE * wave + i, NBLK - 1) * 1024);
+            }
         }
     };
     auto wait_tiles = [&](int newer) {               // all but the `newer` most recent tiles landed
@@ -222,6 +231,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
     float R = -INFINITY, l_run = 0.f;
+    i32x8 pop = {0, 0, 0, 0, 0, 0, 0, 0};          // the tile's E4M3 weights (P.V B operand)
 
     // score A operand: K row 32 blk + l32, bytes 64 ks + 32 hh
     const int k_lane = 16 * (kslot(l32) + 2 * hh);
@@ -264,17 +274,23 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
             sacc[1] = mfma8_last(a3, qop[1], sacc[1]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // element i of block blk is key ts + 32 blk + 8 (i/4) + 4 hh + i%4 of row `row`
+        // element i of block blk is key ts + 4 hh + e of row `row`, e = 32 blk
+        // + 8 (i/4) + i%4.  The visible keys of the row (below T, at or before
+        // the row when causal, within the window) are one range [lo, lo +
+        // width) of e, so one unsigned compare per element tests it.
         if (tile_needs_mask(t)) {
+            const int base = ts + 4 * hh;
+            const int diff = row - base;
+            int e_hi = min(T - base, BN);
+            if (p.causal) e_hi = min(e_hi, diff + 1);
+            const int lo = p.window > 0 ? min(max(diff - p.window + 1, 0), BN) : 0;
+            const uint32_t width = (uint32_t)max(e_hi - lo, 0);
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int key = ts + 32 * blk + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    bool vis = key < T;
-                    if (p.causal) vis = vis && key <= row;
-                    if (p.window > 0) vis = vis && row - key < p.window;
-                    sacc[blk][i] = vis ? sacc[blk][i] : -INFINITY;
+                    const int e = 32 * blk + 8 * (i >> 2) + (i & 3);
+                    sacc[blk][i] = (uint32_t)(e - lo) < width ? sacc[blk][i] : -INFINITY;
                 }
         }
         const int st0 = ts / 32;
@@ -327,11 +343,10 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
             take_weights();
         }
         l_run += sum0 * __builtin_amdgcn_rcpf(448.0f * sv0) + sum1 * __builtin_amdgcn_rcpf(448.0f * sv1);
-        i32x8 pop;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            pop[k] = pack_fp8x4(wt[0][4 * k], wt[0][4 * k + 1], wt[0][4 * k + 2], wt[0][4 * k + 3]);
-            pop[4 + k] = pack_fp8x4(wt[1][4 * k], wt[1][4 * k + 1], wt[1][4 * k + 2], wt[1][4 * k + 3]);
+            pop[k] = pack_fp8x4(wt[0][4 * k], wt[0][4 * k + 1], wt[0][4 * k + 2], wt[0][4 * k + 3], pop[k]);
+            pop[4 + k] = pack_fp8x4(wt[1][4 * k], wt[1][4 * k + 1], wt[1][4 * k + 2], wt[1][4 * k + 3], pop[4 + k]);
         }
         __builtin_amdgcn_sched_barrier(0);
 
