@@ -8,8 +8,9 @@ against fp64, the output's bf16 rounding, and the FP8 matrix instruction's
 accumulation error, which can round a weight to the neighbouring E4M3 code:
 the bar is the FP8 attention bar of tests/parity.py.  Cases: one tile,
 several tiles with a ragged tail, GQA / MHA / MQA, windows, bidirectional,
-T = 1, sink logits, and the Llama-3-8B shape at full size on a synthetic
-FP8 input (sampled rows of every head, the benchmark's launch
+T = 1, sink logits, a head long enough to run past the kernel's table of
+per-key-block constants, and the Llama-3-8B shape at full size on a
+synthetic FP8 input (sampled rows of every head, the benchmark's launch
 configuration).
 """
 import math
@@ -116,3 +117,22 @@ def test_full_size_llama3_sampled_rows(ta, oracle_mod):
                                     scale=s.scale, rows=rows)
     assert_fp8_attention_close(np32(o[:, :, rows]), ro, _vmax(h[4], h[5]), "full prefill fp8")
     assert_lse_close(np32(lse[:, :, rows]), rl, LSE_BF16_ABS, "full prefill fp8 LSE")
+
+
+def test_long_head_past_the_block_table(ta, oracle_mod):
+    """One causal head of T = 64 x 2051 + 8 positions: the last workgroup's
+    tiles (up to 2,052) run past the kernel's table of per-key-block constants
+    (4,096 blocks of 32 keys), which it fills once per workgroup, so its last
+    tiles take the constants per tile; the workgroup before it ends exactly at
+    the table's last entry.  Rows on both sides of those boundaries, a ragged
+    tail, and early rows."""
+    T = 64 * 2051 + 8
+    qkv = _quantised(oracle_mod, 1, T, 1, 1, seed=970)
+    scale = 1.0 / math.sqrt(128)
+    print(f"[case] prefill fp8 long head T={T}", flush=True)
+    o, lse = _run(ta, qkv, causal=True, window=0, scale=scale)
+    rows = [0, 5, 70000, 130815, 130816, 131000, 131071, 131072, 131100, 131200, T - 2, T - 1]
+    (q8, qs), (k8, ks), (v8, vs) = qkv
+    ro, rl = oracle_mod.prefill_fp8(q8, qs, k8, ks, v8, vs, causal=True, scale=scale, rows=rows)
+    assert_fp8_attention_close(np32(o[:, :, rows]), ro, _vmax(v8, vs), "long head fp8 O")
+    assert_lse_close(np32(lse[:, :, rows]), rl, LSE_BF16_ABS, "long head fp8 LSE")

@@ -57,7 +57,13 @@ constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
 constexpr int NBLK = STAGE_BYTES / 1024;      // 21 one-KB copies per tile
 constexpr int PER_WAVE = (NBLK + NW - 1) / NW; // 3 (the last wave repeats its final block)
 constexpr int NSTAGE = 4;
-constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;   // 86016
+constexpr int RING_BYTES = NSTAGE * STAGE_BYTES;  // 86016
+// Per-key-block constants of a workgroup's tiles (k scale, log2 of the v
+// scale, 1 / (448 v scale)), computed once before the tile loop: up to
+// TAB_CAP blocks of 32 keys; tiles past them take the constants per tile.
+constexpr int TAB_CAP = 4096;
+constexpr int LDS_BYTES = RING_BYTES + TAB_CAP * 16;   // 151552
+static_assert(LDS_BYTES <= 160 * 1024, "LDS ring and block table exceed the LDS");
 constexpr float LOG2_448 = 8.807354922057604f;
 constexpr float HEADROOM = 5.0f;
 
@@ -225,6 +231,17 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
     }
     const float a_row = wave_active ? p.scale_log2 * p.qs[((size_t)b * p.hq + h) * p.nt + rw0 / 32] : 0.f;
 
+    // The key-block constants of this workgroup's tiles, block j = key block
+    // 2 t_begin + j; a block past the head's end repeats its last block (its
+    // keys are masked, and it is then the tile's first block).
+    float4 *stab = reinterpret_cast<float4 *>(smem + RING_BYTES);
+    const int n_tab = min(2 * (t_end - t_begin), TAB_CAP);
+    for (int j = tid; j < n_tab; j += 64 * NW) {
+        const int kb = min(2 * t_begin + j, p.nt - 1);
+        const float skj = ksg[kb], svj = vsg[kb];
+        stab[j] = float4{skj, __log2f(svj), __builtin_amdgcn_rcpf(448.0f * svj), 0.f};
+    }
+
     f32x16 oacc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -293,13 +310,28 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
                     sacc[blk][i] = (uint32_t)(e - lo) < width ? sacc[blk][i] : -INFINITY;
                 }
         }
-        const int st0 = ts / 32;
-        const float sk0 = ld_uniform_f(ksg, st0), sv0 = ld_uniform_f(vsg, st0);
-        const bool two = ts + 32 < T;
-        const float sk1 = two ? ld_uniform_f(ksg, st0 + 1) : sk0;
-        const float sv1 = two ? ld_uniform_f(vsg, st0 + 1) : sv0;
-        const float A0 = a_row * sk0, A1 = a_row * sk1;
-        const float lb0 = __log2f(sv0), lb1 = __log2f(sv1);
+        float A0, A1, lb0, lb1, r0, r1;
+        if (2 * rel + 1 < TAB_CAP) {                 // wave-uniform
+            const float4 e0 = stab[2 * rel], e1 = stab[2 * rel + 1];
+            A0 = a_row * e0.x;
+            A1 = a_row * e1.x;
+            lb0 = e0.y;
+            lb1 = e1.y;
+            r0 = e0.z;
+            r1 = e1.z;
+        } else {
+            const int st0 = ts / 32;
+            const float sk0 = ld_uniform_f(ksg, st0), sv0 = ld_uniform_f(vsg, st0);
+            const bool two = ts + 32 < T;
+            const float sk1 = two ? ld_uniform_f(ksg, st0 + 1) : sk0;
+            const float sv1 = two ? ld_uniform_f(vsg, st0 + 1) : sv0;
+            A0 = a_row * sk0;
+            A1 = a_row * sk1;
+            lb0 = __log2f(sv0);
+            lb1 = __log2f(sv1);
+            r0 = __builtin_amdgcn_rcpf(448.0f * sv0);
+            r1 = __builtin_amdgcn_rcpf(448.0f * sv1);
+        }
         // The weights against the current reference.  They are positive, so
         // a lane whose weights sum to at most 448 has none above 448, i.e. no
         // y above R: only when some lane's sum passes 448 (or a row's R is
@@ -342,7 +374,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
             }
             take_weights();
         }
-        l_run += sum0 * __builtin_amdgcn_rcpf(448.0f * sv0) + sum1 * __builtin_amdgcn_rcpf(448.0f * sv1);
+        l_run += sum0 * r0 + sum1 * r1;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             pop[k] = pack_fp8x4(wt[0][4 * k], wt[0][4 * k + 1], wt[0][4 * k + 2], wt[0][4 * k + 3], pop[k]);
