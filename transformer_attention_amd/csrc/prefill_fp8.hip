@@ -63,6 +63,7 @@ constexpr int RING_BYTES = NSTAGE * STAGE_BYTES;  // 86016
 // TAB_CAP blocks of 32 keys; tiles past them take the constants per tile.
 constexpr int TAB_CAP = 4096;
 constexpr int LDS_BYTES = RING_BYTES + TAB_CAP * 16;   // 151552
+static_assert(NW * 32 * 144 <= RING_BYTES, "epilogue staging exceeds the ring");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring and block table exceed the LDS");
 constexpr float LOG2_448 = 8.807354922057604f;
 constexpr float HEADROOM = 5.0f;
@@ -401,9 +402,15 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    // Every wave is past the tile loop and no copy is in flight: the output
+    // goes out through the ring, so that each store writes a whole 128-byte
+    // row half.  Each lane holds four-value pieces of its row; the wave's 32
+    // rows x 64 values of one half go to its own region (rows 144 bytes
+    // apart: the 8-byte writes of a quarter wave hit distinct banks) and come
+    // back as 16 bytes of 8 consecutive values per lane, 8 lanes per row half.
+    raw_barrier();
     if (!wave_active) return;
     const float lt = pair32_sum(l_run);
-    if (row >= T) return;
     float inv = lt > 0.f ? 1.0f / (448.0f * lt) : 0.f;
     float lse_nat = lt > 0.f ? (R + __log2f(lt)) * kLn2 : -INFINITY;
     if (p.sinks) {
@@ -411,17 +418,27 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
         inv = finish_row_with_sink(lt > 0.f ? R : -INFINITY, lt, p.sinks[h] * kLog2e, ls) * (1.0f / 448.0f);
         lse_nat = ls;
     }
-    __bf16 *orow = p.o + q_base + (size_t)row * D;
+    char *reg = smem + wave * (32 * 144);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int d = 32 * db + 8 * q4 + 4 * hh;
-            u32x2 w = {pack_bf16x2(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv),
-                       pack_bf16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv)};
-            *reinterpret_cast<u32x2 *>(orow + d) = w;
+        for (int db = 2 * half; db < 2 * half + 2; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = 32 * db + 8 * q4 + 4 * hh - 64 * half;
+                u32x2 w = {pack_bf16x2(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv),
+                           pack_bf16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(reg + l32 * 144 + 2 * d) = w;
+            }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = 8 * r + (lane >> 3), ch = lane & 7;
+            const u32x4 v4 = *reinterpret_cast<const u32x4 *>(reg + rr * 144 + 16 * ch);
+            if (rw0 + rr < T)
+                *reinterpret_cast<u32x4 *>(p.o + q_base + (size_t)(rw0 + rr) * D + 64 * half + 8 * ch) = v4;
         }
-    if (p.lse && hh == 0) p.lse[((size_t)b * p.hq + h) * (size_t)T + row] = lse_nat;
+    }
+    if (p.lse && hh == 0 && row < T) p.lse[((size_t)b * p.hq + h) * (size_t)T + row] = lse_nat;
 }
 
 }  // namespace
