@@ -202,7 +202,10 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
             for (int i = 0; i < PER_WAVE; ++i)
                 dma16_off_at(dma_v[i] ? vb0 : kb0, dma_off[i], stage + min(PER_WAVE * wave + i, NBLK - 1) * 1024);
         } else {                                     // ragged last tile: rows past T re-read row T-1
-            const int last = T - 1 - ts;
+            // (opaque to the compiler: as an affine function of the tile it
+            // was strength-reduced into per-lane counters updated every tile)
+            int last = T - 1 - ts;
+            asm volatile("" : "+s"(last));
 #pragma unroll
             for (int i = 0; i < PER_WAVE; ++i) {
                 const uint32_t off = dma_row[i] > last
@@ -297,7 +300,9 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
         // the row when causal, within the window) are one range [lo, lo +
         // width) of e, so one unsigned compare per element tests it.
         if (tile_needs_mask(t)) {
-            const int base = ts + 4 * hh;
+            int tsm = ts;                            // opaque, as for the ragged copy offsets
+            asm volatile("" : "+s"(tsm));
+            const int base = tsm + 4 * hh;
             const int diff = row - base;
             int e_hi = min(T - base, BN);
             if (p.causal) e_hi = min(e_hi, diff + 1);
@@ -344,14 +349,12 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_fp8_d128_kernel(Params p) 
         auto take_weights = [&]() {
             const float R_use = R == -INFINITY ? 0.f : R;
             const float bb0 = lb0 + LOG2_448 - R_use, bb1 = lb1 + LOG2_448 - R_use;
-            sum0 = 0.f;
-            sum1 = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 wt[0][i] = fast_exp2(__builtin_fmaf(sacc[0][i], A0, bb0));
                 wt[1][i] = fast_exp2(__builtin_fmaf(sacc[1][i], A1, bb1));
-                sum0 += wt[0][i];
-                sum1 += wt[1][i];
+                sum0 = i == 0 ? wt[0][0] : sum0 + wt[0][i];
+                sum1 = i == 0 ? wt[1][0] : sum1 + wt[1][i];
             }
         };
         take_weights();
