@@ -123,8 +123,11 @@ __device__ __forceinline__ i32x8 lds32(const char *p) {       // 32 bytes as two
 
 // four E4M3 codes of a, b, c, d (bytes 0..3, round to nearest even; the
 // callers' values are at most 448 * (1 + 2^-20), which rounds to 448)
-__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+// Four E4M3 codes in one word.  The first conversion writes the low half and
+// keeps the high half of `old`, which the second then overwrites: passing the
+// word's previous contents (rather than 0) spares a register clear per word.
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d, int old) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -175,7 +178,11 @@ void mla_decode_fp8_kernel(Params p) {
         char *stage = smem + (t % NSTAGE) * TILE_BYTES;
         const int t0 = lo + t * TB;
         const uint8_t *gbase = cg + (size_t)t0 * ROWS;
-        const int last = hi_tok - 1 - t0;           // last valid row of this tile
+        // last valid row of this tile (opaque to the compiler: as an affine
+        // function of the tile it was strength-reduced into per-lane counters
+        // updated every tile)
+        int last = hi_tok - 1 - t0;
+        asm volatile("" : "+s"(last));
         if (last >= TB - 1) {
 #pragma unroll
             for (int i = 0; i < 10; ++i) {
@@ -222,6 +229,7 @@ void mla_decode_fp8_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
     float R = -INFINITY, l_run = 0.f;
+    i32x8 pop = {0, 0, 0, 0, 0, 0, 0, 0};          // the tile's E4M3 weights (P.V B operand)
 
     // Score A operand: row 32 blk + l32, bytes 64 ks + 32 hh .. +31.
     const char *srow = smem + 16 * (row_slot(l32) + 2 * hh);
@@ -312,20 +320,20 @@ void mla_decode_fp8_kernel(Params p) {
         const float R_use = R == -INFINITY ? 0.f : R;
         const float bb0 = lb0 + LOG2_448 - R_use, bb1 = lb1 + LOG2_448 - R_use;
         // (computed in place: sacc[blk][i] becomes the weight of score i)
-        float sum0 = 0.f, sum1 = 0.f;
+        float sum0, sum1;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             sacc[0][i] = fast_exp2(__builtin_fmaf(sacc[0][i], A0, bb0));
             sacc[1][i] = fast_exp2(__builtin_fmaf(sacc[1][i], A1, bb1));
-            sum0 += sacc[0][i];
-            sum1 += sacc[1][i];
+            sum0 = i == 0 ? sacc[0][0] : sum0 + sacc[0][i];
+            sum1 = i == 0 ? sacc[1][0] : sum1 + sacc[1][i];
         }
         l_run += sum0 * __builtin_amdgcn_rcpf(448.0f * sc0) + sum1 * __builtin_amdgcn_rcpf(448.0f * sc1);
-        i32x8 pop;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            pop[k] = pack_fp8x4(sacc[0][4 * k], sacc[0][4 * k + 1], sacc[0][4 * k + 2], sacc[0][4 * k + 3]);
-            pop[4 + k] = pack_fp8x4(sacc[1][4 * k], sacc[1][4 * k + 1], sacc[1][4 * k + 2], sacc[1][4 * k + 3]);
+            pop[k] = pack_fp8x4(sacc[0][4 * k], sacc[0][4 * k + 1], sacc[0][4 * k + 2], sacc[0][4 * k + 3], pop[k]);
+            pop[4 + k] = pack_fp8x4(sacc[1][4 * k], sacc[1][4 * k + 1], sacc[1][4 * k + 2], sacc[1][4 * k + 3],
+                                    pop[4 + k]);
         }
         __builtin_amdgcn_sched_barrier(0);
 
