@@ -17,7 +17,9 @@ tile boundary, a window shorter than a tile, a short split) is still met:
 * the prefill backward: batch 1-2, lengths up to 400, group sizes 1-4, causal
   with or without a window, or bidirectional;
 * the FP8 prefill: the prefill's shape space at lengths up to 400, against the
-  oracle's FP8 recipe.
+  oracle's FP8 recipe;
+* the FP8-cache decode, the paged decode (pages of 32-256 positions, lengths
+  at and just past a page) and the FP8 MLA decode in the same way.
 
 The bars are those of the other files (tests/parity.py).
 """
@@ -234,3 +236,102 @@ def test_prefill_fp8_random(ta, oracle_mod, B, T, hq, hkv, causal, window):
     vmax = float(np.abs(vals * np.repeat(vs, 32, axis=-1)[..., :T, None]).max())
     assert_fp8_attention_close(np32(o), ro, vmax, "prefill fp8 O")
     assert_lse_close(np32(lse), rl, LSE_BF16_ABS, "prefill fp8 LSE")
+
+
+FP8_DECODE = [c[:7] for c in _decode_cases(16)]
+
+
+@pytest.mark.parametrize("B,S_max,hq,hkv,lens,window,split", FP8_DECODE)
+def test_decode_fp8_random(ta, oracle_mod, B, S_max, hq, hkv, lens, window, split):
+    g = torch.Generator().manual_seed(S_max * 37 + hq * 11 + hkv + B)
+    q = _bf16(g, B, hq, 1, 128)
+    k8, ks = oracle_mod.quantize_kv_fp8(np32(_bf16(g, B, hkv, S_max, 128)))
+    v8, vs = oracle_mod.quantize_kv_fp8(np32(_bf16(g, B, hkv, S_max, 128)))
+    for b, n in enumerate(lens):                     # never read: positions >= len
+        k8[b, :, n:] = 0x7f
+        v8[b, :, n:] = 0xff
+        ks[b, :, (n + 31) // 32:] = np.nan
+        vs[b, :, (n + 31) // 32:] = np.nan
+    scale = 1.0 / math.sqrt(128)
+    print(f"[case] fp8 decode {B},{S_max},{hq},{hkv},{lens},{window},{split}", flush=True)
+    dev = [torch.from_numpy(x).cuda() for x in (k8, v8, ks, vs)]
+    o, lse = ta.attn_decode_fp8(q.cuda(), *dev, torch.tensor(lens, dtype=torch.int32).cuda(),
+                                window=window, scale=scale, split_tokens=split, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mod.decode_fp8(np32(q), k8, v8, ks, vs, np.array(lens, np.int32), window=window,
+                                   scale=scale)
+    assert_bf16_close(np32(o)[:, :, 0], ro, "fp8 decode O")
+    assert_lse_close(np32(lse), rl, LSE_BF16_ABS, "fp8 decode LSE")
+
+
+def _paged_cases(n):
+    out = []
+    for _ in range(n):
+        B = int(_R.randint(1, 5))
+        page = int(_R.choice([32, 64, 96, 128, 256]))
+        S_max = page * int(_R.randint(1, 1200 // page + 1))
+        hq, hkv = _heads(max_g=16, max_hq=64)
+        lens = [int(_R.choice([1, S_max, page, min(S_max, page + 1), _R.randint(1, S_max + 1)]))
+                for _ in range(B)]
+        window = 0 if _R.rand() < 0.6 else int(_R.randint(1, S_max + 1))
+        split = int(_R.choice([0, 0, 64, 128, 256]))
+        out.append((B, S_max, hq, hkv, page, lens, window, split))
+    return out
+
+
+PAGED = _paged_cases(12)
+
+
+@pytest.mark.parametrize("B,S_max,hq,hkv,page,lens,window,split", PAGED)
+def test_decode_paged_random(ta, oracle_mod, B, S_max, hq, hkv, page, lens, window, split):
+    import workloads as W
+    g = torch.Generator().manual_seed(S_max * 41 + hq * 13 + hkv + page)
+    q = _bf16(g, B, hq, 1, 128).cuda()
+    kc, vc = _bf16(g, B, hkv, S_max, 128), _bf16(g, B, hkv, S_max, 128)
+    for b, L in enumerate(lens):
+        kc[b, :, L:] = float("nan")
+        vc[b, :, L:] = float("nan")
+    kp, table = W.paged_layout(kc.cuda(), page, seed=S_max + B, extra_pages=2)
+    vp, _ = W.paged_layout(vc.cuda(), page, seed=S_max + B, extra_pages=2)
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    scale = 1.0 / math.sqrt(128)
+    print(f"[case] paged decode {B},{S_max},{hq},{hkv},ps={page},{lens},{window},{split}", flush=True)
+    o, lse = ta.attn_decode_paged(q, kp, vp, lens_t.cuda(), table, window=window, scale=scale,
+                                  split_tokens=split, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mod.decode_paged(np32(q), np32(kp), np32(vp), table.cpu().numpy(), lens_t.numpy(),
+                                     window=window, scale=scale)
+    assert_bf16_close(np32(o)[:, :, 0], ro, "paged decode O")
+    assert_lse_close(np32(lse), rl, LSE_BF16_ABS, "paged decode LSE")
+
+
+MLA_FP8 = _mla_cases(8)
+
+
+@pytest.mark.parametrize("B,S_max,H,lens,split", MLA_FP8)
+def test_mla_fp8_random(ta, oracle_mod, B, S_max, H, lens, split):
+    g = torch.Generator().manual_seed(S_max * 43 + H + B)
+    q = _bf16(g, B, H, 576)
+    codes, scales = oracle_mod.quantize_kv_fp8(np32(_bf16(g, B, S_max, 576))[:, None])
+    codes, scales = codes[:, 0], scales[:, 0]
+    for b, n in enumerate(lens):                     # never read: positions >= len
+        codes[b, n:] = 0x7f
+        scales[b, (n + 31) // 32:] = np.nan
+    lens_np = np.array(lens, np.int32)
+    scale = 1.0 / math.sqrt(192.0)
+    print(f"[case] mla fp8 {B},{S_max},{H},{lens},{split}", flush=True)
+    o, lse = ta.mla_decode_fp8(q.cuda(), torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                               torch.from_numpy(lens_np).cuda(), scale=scale, split_tokens=split,
+                               return_lse=True)
+    torch.cuda.synchronize()
+    eff = split
+    if split == 0:                                   # the library's choice (as in mla_decode_fp8)
+        eff = (S_max * B * ((H + 127) // 128) + 255) // 256
+        eff = min(max(64, (eff + 63) // 64 * 64), (S_max + 63) // 64 * 64)
+    ro, rl = oracle_mod.mla_decode_fp8(np32(q), codes, scales, lens_np, d_c=512, d_r=64, scale=scale,
+                                       split=eff)
+    vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    vmax = max([float(np.abs(vals[codes[b, :n, :512]] * np.repeat(scales[b], 32)[:n, None]).max())
+                for b, n in enumerate(lens) if n] + [0.0])
+    assert_fp8_attention_close(np32(o), ro, vmax, "mla fp8 O")
+    assert_lse_close(np32(lse), rl, LSE_BF16_ABS, "mla fp8 LSE")
