@@ -40,7 +40,10 @@
 //    the same tiles as with the max taken every time;
 //  * LDS rows: K at slot 8 r + r/2 (16-row score reads of a quarter wave hit
 //    16 distinct slots), V at slot 12 r + (r/4) mod 4 (the 8-row transposing
-//    reads of a half wave hit 16 distinct slots).
+//    reads of a half wave hit 16 distinct slots);
+//  * after the ring, a table of the workgroup's per-key-block constants (k
+//    scale, log2 of the v scale, 1 / (448 v scale)), filled once before the
+//    tile loop; the output leaves through the ring as whole row halves.
 #include "kcommon.h"
 #include "kernels.h"
 
