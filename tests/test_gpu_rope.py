@@ -20,8 +20,7 @@ def ta():
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-# d = 132 is not a multiple of 8: the pair-per-thread kernel (bf16 too);
-# 11 query heads: one full and one partial batch of 8 in the vector kernel.
+# Odd head counts (11 / 3) and a 132-wide row, besides the two head sizes.
 @pytest.mark.parametrize("B,T,hq,hk,d,base", [(2, 300, 8, 2, 128, 5e5), (1, 77, 4, 4, 64, 1e4),
                                              (1, 50, 11, 3, 64, 1e4), (1, 33, 3, 1, 132, 1e4)])
 def test_rope_prefill_shapes(ta, oracle_mod, dtype, B, T, hq, hk, d, base):
