@@ -48,6 +48,10 @@ F32_CASES = [
     (1, 130, 2, 2, 64, True, 17),
     (1, 77, 4, 2, 128, False, 0),
     (3, 1, 2, 1, 16, True, 0),
+    # d <= 32: each row's keys split over four waves, then merged
+    (1, 300, 4, 2, 16, True, 50),    # several 128-key tiles, window
+    (2, 200, 2, 1, 32, False, 0),    # several 64-key tiles, bidirectional
+    (1, 129, 2, 2, 16, True, 0),     # one key past the first tile
 ]
 
 
