@@ -6,9 +6,10 @@
 // the FlashAttention-2 recurrence) -- but with fp32 FMAs throughout so that
 // fp32 inputs keep fp32 accuracy.  A workgroup covers 64 rows of one query
 // head and reads the K/V head h / (h_q / h_kv).  For d_h <= 32 each row's
-// keys are split over 4 waves (wave w takes keys w, w + 4, ... of every
-// tile), each with its own running (m, l, O); at the end the four states of
-// a row merge through LDS as the FlashAttention-2 state merge prescribes
+// keys are split over NSPLIT waves (8 for d_h = 16, 4 for d_h = 32; wave w
+// takes keys w, w + NSPLIT, ... of every tile), each with its own running
+// (m, l, O); at the end the states of a row merge through LDS as the
+// FlashAttention-2 state merge prescribes
 // (the same section: rescale each by 2^(m_w - M), add).  For larger heads
 // one wave owns the row.  Each dot product runs as four interleaved FMA
 // chains.  This path serves small fp32 problems, where the time is latency:
@@ -33,7 +34,7 @@ struct Params {
 };
 
 template <int DH> struct Shape {
-    static constexpr int NSPLIT = DH <= 32 ? 4 : 1;              // waves sharing a row's keys
+    static constexpr int NSPLIT = DH == 16 ? 8 : (DH == 32 ? 4 : 1);   // waves sharing a row's keys
     static constexpr int TK = DH == 16 ? 128 : (DH == 32 ? 64 : 32);   // keys per LDS tile
 };
 
